@@ -1,0 +1,227 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) Gated DeltaNet layer hot path.
+ *
+ * The library (libgdn.so) runs every stage as a hand-written HIP kernel:
+ *   1. exact token chunks for the conv          gdn_make_chunks / _device
+ *   2. width-4 depthwise causal conv             gdn_causal_conv_fwd
+ *   3. SiLU + q|k|v split + per-head L2 norm     gdn_postconv_l2
+ *   4. chunked gated delta-rule prefill          gdn_delta_rule_prefill
+ *   5. per-token decode / verify step            gdn_delta_rule_step
+ *   6. layer-batched commit of a verify window   gdn_commit
+ *
+ * Sources (page title, section):
+ *   "perf(gdn): optimize post-conv and causal-conv kernels" (vllm.cpp pull
+ *   request 155): "Blocker" (conv over c channels with k = 4 taps, row
+ *   padding), "What I verified" and "The one thing I changed in your tests"
+ *   (post-conv L2 reduction and its float32 output arm), "New issue #305"
+ *   (first chunk reads, last chunk writes conv_state; has_initial_state).
+ *   "Strata pull request 3226": "Problem and result" and "Summary" items 1-4
+ *   (verify forward with commit_state = false, per-token state-resident step,
+ *   layer-batched commit of n_keep tokens by state replay).
+ *   The recurrence is the gated delta rule
+ *       S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t
+ *   (Yang, Kautz, Hatamizadeh, "Gated Delta Networks", 2024).
+ *
+ * Conventions shared by every call
+ *   - Pointers marked (device) are device memory; (host) is host memory.
+ *     The caller owns every buffer.  The library allocates nothing, keeps no
+ *     state between calls and is safe to call from several host threads.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  A returned GDN_OK means the launch was accepted.
+ *   - Activations are float32 (GDN_F32) or bfloat16 (GDN_BF16); conv weights,
+ *     gates and both states are float32.  Head sizes dk = dv = 128.
+ *   - Packed channels: C = 2*Hk*dk + Hv*dv, laid out q | k | v.  v-head h
+ *     reads k-head h / (Hv/Hk).
+ *   - Varlen batches: cu_seqlens[nseq+1] (device, int32) with cu[0] = 0,
+ *     nondecreasing, cu[nseq] = N.  Device-resident integers are
+ *     preconditions: they are not read back on the host.
+ *   - has_initial_state[nseq] (device, uint8; NULL = all set): when 0, the
+ *     sequence starts from zero conv rows and a zero recurrent state, and
+ *     the stored buffers are not read (they may hold anything, NaN included).
+ *   - Errors: the host validates arguments before any launch and returns a
+ *     gdn_status; gdn_last_error() gives a message (thread-local).  No
+ *     exception crosses the ABI.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,      /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,     /* sizes out of range or inconsistent */
+  GDN_ERR_DTYPE = 3,     /* unsupported dtype code */
+  GDN_ERR_ALIGN = 4,     /* a pointer or row stride is not 16-byte aligned */
+  GDN_ERR_ALIAS = 5,     /* an output overlaps an input it must not overlap */
+  GDN_ERR_LAUNCH = 6,    /* the HIP runtime rejected a launch */
+  GDN_ERR_CAPACITY = 7   /* an output array is too small */
+} gdn_status;
+
+/* One exact conv chunk: tokens [begin, end) of sequence `seq` (global token
+ * indices).  flags: GDN_CHUNK_FIRST = the sequence's first chunk (its window
+ * reaches into conv_state), GDN_CHUNK_LAST = the sequence's last chunk.
+ * seq = -1 marks an unused slot (written by gdn_make_chunks_device). */
+typedef struct {
+  int32_t seq, begin, end, flags;
+} gdn_chunk;
+
+#define GDN_CHUNK_FIRST 1
+#define GDN_CHUNK_LAST 2
+#define GDN_CHUNK_LEN 64
+
+/* One layer's tensors for gdn_commit (all device pointers).  `x`, `k`, `v`,
+ * `g`, `beta` are the exact tensors the verify forward consumed for this
+ * layer; `conv_state` and `state` are updated in place. */
+typedef struct {
+  const void* x;          /* conv input  [N][x_row_stride] activations */
+  int64_t x_row_stride;   /* elements, >= C */
+  float* conv_state;      /* [nseq][3][C] */
+  float* state;           /* [nseq][Hv][dv][dk] */
+  const void* k;          /* post-conv k_hat [N][Hk][dk] activations */
+  const void* v;          /* post-conv v     [N][Hv][dv] activations */
+  const float* g;         /* [N][Hv]  log of the decay gate a_t */
+  const float* beta;      /* [N][Hv]  b_t */
+} gdn_layer_io;
+
+/* ---- library info ------------------------------------------------------ */
+
+int gdn_abi_version(void);
+const char* gdn_status_string(int status);
+/* Message for the last non-OK status returned on this host thread. */
+const char* gdn_last_error(void);
+
+/* ---- 1. exact token chunks ---------------------------------------------
+ * Cuts every sequence into consecutive chunks of `chunk_len` tokens, the
+ * last one possibly shorter, ordered by sequence then position; empty
+ * sequences emit nothing ("New issue #305": exact chunks, first-chunk /
+ * last-chunk roles).  Integer work, bit-exact.
+ *
+ * gdn_chunk_capacity: an upper bound on the number of chunks of any batch
+ * with N tokens in nseq sequences: floor((N + nseq*(chunk_len-1)) /
+ * chunk_len).
+ *
+ * gdn_make_chunks (host): reads cu_seqlens (host, nseq+1 entries), writes
+ * at most `cap` descriptors to out (host).  Returns the count (>= 0), or
+ * -GDN_ERR_* (NULL pointer, nseq < 0, chunk_len < 1, cu not nondecreasing
+ * from 0, or more than cap chunks).
+ *
+ * gdn_make_chunks_device: the same list built on the GPU from a device
+ * cu_seqlens, written to out (device) with exactly `cap` slots; slots past
+ * the real count get seq = -1.  cap must be >= gdn_chunk_capacity(N, nseq,
+ * chunk_len) for the batch (precondition).  One small launch. */
+int gdn_chunk_capacity(int N, int nseq, int chunk_len);
+int gdn_make_chunks(const int32_t* cu_seqlens, int nseq, int chunk_len,
+                    gdn_chunk* out, int cap);
+int gdn_make_chunks_device(const int32_t* cu_seqlens, int nseq, int chunk_len,
+                           gdn_chunk* out, int cap, void* stream);
+
+/* ---- 2. causal conv -----------------------------------------------------
+ * Width-4 depthwise causal conv1d over the packed channels ("Blocker":
+ * c channels, k = 4 taps; "New issue #305"):
+ *   y[t][c] = bias[c] + sum_{j=0..3} w[c][j] * xe[t-3+j][c]
+ * where xe is the sequence's input preceded by its 3 stored conv rows
+ * (row 0 oldest; zeros when has_initial_state is 0).  Tap w[c][3]
+ * multiplies the current token.
+ * When write_state != 0, conv_state[s] becomes the last 3 rows of
+ * [stored rows ; x of sequence s]; otherwise conv_state is not written.
+ * One workgroup per (chunk, 2048-channel group) owns each sequence's
+ * conv_state: the first chunk's workgroup reads the stored rows and, later
+ * in the same threads' program order, writes the final rows, so the
+ * in-place update has no cross-workgroup race.
+ *   x           (device) [N][x_row_stride] act, x_row_stride >= C, rows
+ *               16-byte aligned
+ *   w           (device) float [C][4];  bias (device) float [C] or NULL (0)
+ *   conv_state  (device) float [nseq][3][C], read and written in place
+ *   chunks      (device) nchunks descriptors (from gdn_make_chunks*);
+ *               unused slots (seq = -1) are skipped
+ *   y           (device) [N][C] act; must not overlap x or conv_state
+ * C must be a multiple of 8. */
+int gdn_causal_conv_fwd(const void* x, int64_t x_row_stride, int act,
+                        const float* w, const float* bias,
+                        float* conv_state, const uint8_t* has_initial_state,
+                        const int32_t* cu_seqlens, const gdn_chunk* chunks,
+                        int nchunks, int nseq, int N, int C, int write_state,
+                        void* y, void* stream);
+
+/* ---- 3. post-conv -------------------------------------------------------
+ * s = SiLU(y) = y / (1 + exp(-y)) on all C channels; split q | k | v; per q
+ * and k head: q_hat = s * (1 / sqrt(sum(s^2) + eps)).  v = s.
+ * ("What I verified", "The one thing I changed in your tests".)
+ * The squared norm is summed in one fixed order: a pairwise tree,
+ * neighbours first (level l adds adjacent blocks of 2^l elements), each
+ * step one float32 addition with no fused multiply-add; float32 sqrt and
+ * division are correctly rounded.  For a float32 output, SiLU is evaluated
+ * in float64 and rounded once to float32.
+ *   y      (device) [N][y_row_stride] act `in`, y_row_stride >= C
+ *   q_out, k_out (device) [N][Hk][dk], v_out [N][Hv][dv], dtype `out`;
+ *          none may overlap y
+ *   eps > 0 (float32). */
+int gdn_postconv_l2(const void* y, int64_t y_row_stride, int in, int N,
+                    int Hk, int Hv, int dk, int dv, float eps,
+                    void* q_out, void* k_out, void* v_out, int out, void* stream);
+
+/* ---- 4. chunked prefill --------------------------------------------------
+ * Gated delta rule over every sequence of a varlen batch in chunks of 64
+ * tokens (chunk-local K K^T and Q K^T on MFMA, unit-lower-triangular solve
+ * for the WY factors, float32 state carried between chunks).  For sequence
+ * s, v-head h (k-head h/(Hv/Hk)), starting from S = state[s][h] (or 0):
+ *   S <- a_t S (I - b_t k k^T) + b_t v k^T,  o_t = S q_t,  a_t = exp(g[t][h])
+ * and the final S is written back to state[s][h] (always).
+ *   q, k   (device) [N][Hk][dk] act;  v (device) [N][Hv][dv] act
+ *   g, beta (device) float [N][Hv]
+ *   state  (device) float [nseq][Hv][dv][dk] (k index fastest), in place
+ *   o      (device) [N][Hv][dv] act; must not overlap any input. */
+int gdn_delta_rule_prefill(const void* q, const void* k, const void* v, int act,
+                           const float* g, const float* beta,
+                           const int32_t* cu_seqlens, int nseq, int N,
+                           int Hk, int Hv, int dk, int dv,
+                           float* state, const uint8_t* has_initial_state,
+                           void* o, void* stream);
+
+/* ---- 5. decode / verify step ---------------------------------------------
+ * The same recurrence token by token with the state held in registers
+ * ("Summary" item 3: state-resident per-token step).  Every sequence's
+ * tokens (a decode token or a window of draft tokens) run in one launch.
+ * commit_state != 0 writes the final S back to state; commit_state == 0
+ * writes no state at all (verify forward; see gdn_commit).
+ * Same operands and layouts as gdn_delta_rule_prefill. */
+int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act,
+                        const float* g, const float* beta,
+                        const int32_t* cu_seqlens, int nseq, int N,
+                        int Hk, int Hv, int dk, int dv,
+                        float* state, const uint8_t* has_initial_state,
+                        void* o, int commit_state, void* stream);
+
+/* ---- 6. layer-batched commit ----------------------------------------------
+ * After a verify window ran with write_state = 0 / commit_state = 0, keep
+ * the first n = n_keep[s] tokens of every sequence in every layer, in ONE
+ * launch ("Problem and result" item 2, "Summary" item 1):
+ *   conv_state[s] <- last 3 rows of [stored rows ; x_0 .. x_{n-1}]
+ *   state[s]      <- the recurrence replayed over those n tokens from the
+ *                    stored state, with the same arithmetic as
+ *                    gdn_delta_rule_step (bitwise equal to a step with
+ *                    commit_state = 1 over the same n tokens)
+ * n = 0 leaves both states bit-identical.
+ *   layers     (device) gdn_layer_io[L]
+ *   cu_seqlens (device) [nseq+1]; n_keep (device) int32 [nseq], 0 <= n_keep[s]
+ *              <= cu[s+1]-cu[s] (precondition)
+ *   has_initial_state (device) uint8 [nseq] or NULL. */
+int gdn_commit(const gdn_layer_io* layers, int L, const int32_t* cu_seqlens,
+               const int32_t* n_keep, const uint8_t* has_initial_state, int nseq,
+               int C, int Hk, int Hv, int dk, int dv, int act, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

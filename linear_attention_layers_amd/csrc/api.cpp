@@ -1,0 +1,219 @@
+// C-ABI entry points of libgdn.so: argument validation, then one launch
+// each.  Declarations and contracts: include/gdn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return GDN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == GDN_F32 ? 4 : 2; }
+
+bool valid_dtype(int d) { return d == GDN_F32 || d == GDN_BF16; }
+
+// [a, a + na) and [b, b + nb) overlap?
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_heads(int Hk, int Hv, int dk, int dv) {
+  if (dk != 128 || dv != 128) return fail(GDN_ERR_SHAPE, "head sizes must be dk = dv = 128 (got %d, %d)", dk, dv);
+  if (Hk < 1 || Hv < 1 || Hv % Hk != 0)
+    return fail(GDN_ERR_SHAPE, "need Hk >= 1 and Hv a multiple of Hk (got Hk=%d Hv=%d)", Hk, Hv);
+  return GDN_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_recurrence(const void* q, const void* k, const void* v, int act, const float* g,
+                     const float* beta, const int32_t* cu, int nseq, int N, int Hk, int Hv,
+                     int dk, int dv, const float* state, const void* o) {
+  if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
+  if (nseq < 0 || N < 0) return fail(GDN_ERR_SHAPE, "negative nseq or N");
+  int st = check_heads(Hk, Hv, dk, dv);
+  if (st != GDN_OK) return st;
+  if (nseq == 0) return GDN_OK;
+  if (!cu || !state) return fail(GDN_ERR_NULL, "cu_seqlens and state are required");
+  if (N > 0 && (!q || !k || !v || !g || !beta || !o)) return fail(GDN_ERR_NULL, "q, k, v, g, beta and o are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
+    return fail(GDN_ERR_ALIGN, "q, k, v, o and state must be 16-byte aligned");
+  const size_t e = elem_bytes(act);
+  const size_t nq = (size_t)N * Hk * dk * e, nv = (size_t)N * Hv * dv * e;
+  const size_t no = (size_t)N * Hv * dv * e, ns = (size_t)nseq * Hv * dv * dk * 4;
+  const size_t ng = (size_t)N * Hv * 4;
+  if (overlaps(o, no, q, nq) || overlaps(o, no, k, nq) || overlaps(o, no, v, nv) ||
+      overlaps(o, no, g, ng) || overlaps(o, no, beta, ng) || overlaps(o, no, state, ns) ||
+      overlaps(state, ns, q, nq) || overlaps(state, ns, k, nq) || overlaps(state, ns, v, nv))
+    return fail(GDN_ERR_ALIAS, "o and state must not overlap q, k, v, g, beta or each other");
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "null pointer";
+    case GDN_ERR_SHAPE: return "bad shape";
+    case GDN_ERR_DTYPE: return "bad dtype";
+    case GDN_ERR_ALIGN: return "misaligned pointer or stride";
+    case GDN_ERR_ALIAS: return "overlapping buffers";
+    case GDN_ERR_LAUNCH: return "launch failed";
+    case GDN_ERR_CAPACITY: return "output capacity too small";
+    default: return "unknown status";
+  }
+}
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+int gdn_chunk_capacity(int N, int nseq, int chunk_len) {
+  if (N < 0 || nseq < 0 || chunk_len < 1) return 0;
+  const long long cap = ((long long)N + (long long)nseq * (chunk_len - 1)) / chunk_len;
+  return cap > 0x7fffffff ? 0x7fffffff : (int)cap;
+}
+
+int gdn_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out, int cap) {
+  if (nseq < 0) return -fail(GDN_ERR_SHAPE, "nseq < 0");
+  if (chunk_len < 1) return -fail(GDN_ERR_SHAPE, "chunk_len < 1");
+  if (cu == nullptr) return -fail(GDN_ERR_NULL, "cu_seqlens is NULL");
+  if (cu[0] != 0) return -fail(GDN_ERR_SHAPE, "cu_seqlens[0] must be 0");
+  int count = 0;
+  for (int s = 0; s < nseq; ++s) {
+    const int b = cu[s], e = cu[s + 1];
+    if (e < b) return -fail(GDN_ERR_SHAPE, "cu_seqlens decreases at %d", s);
+    for (int j = 0, t = b; t < e; ++j, t += chunk_len) {
+      if (count >= cap) return -fail(GDN_ERR_CAPACITY, "more than %d chunks", cap);
+      if (out == nullptr) return -fail(GDN_ERR_NULL, "out is NULL");
+      gdn_chunk& c = out[count++];
+      c.seq = s;
+      c.begin = t;
+      c.end = (e - t < chunk_len) ? e : t + chunk_len;
+      c.flags = (j == 0 ? GDN_CHUNK_FIRST : 0) | (c.end == e ? GDN_CHUNK_LAST : 0);
+    }
+  }
+  return count;
+}
+
+int gdn_make_chunks_device(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out, int cap,
+                           void* stream) {
+  if (nseq < 0 || cap < 0) return -fail(GDN_ERR_SHAPE, "nseq or cap < 0");
+  if (chunk_len < 1) return -fail(GDN_ERR_SHAPE, "chunk_len < 1");
+  if (cap == 0) return GDN_OK;
+  if (cu == nullptr || out == nullptr) return -fail(GDN_ERR_NULL, "cu_seqlens and out are required");
+  const int st = launched(gdn::launch_make_chunks(cu, nseq, chunk_len, out, cap, as_stream(stream)),
+                          "make_chunks");
+  return st == GDN_OK ? GDN_OK : -st;
+}
+
+int gdn_causal_conv_fwd(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                        float* conv_state, const uint8_t* has_init, const int32_t* cu,
+                        const gdn_chunk* chunks, int nchunks, int nseq, int N, int C,
+                        int write_state, void* y, void* stream) {
+  if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
+  if (N < 0 || nseq < 0 || nchunks < 0 || C < 8 || C % 8 != 0 || xs < C)
+    return fail(GDN_ERR_SHAPE, "need N, nseq, nchunks >= 0, C a positive multiple of 8, x_row_stride >= C");
+  if (N == 0 || nseq == 0 || nchunks == 0) return GDN_OK;
+  if (!x || !w || !conv_state || !cu || !chunks || !y) return fail(GDN_ERR_NULL, "missing required pointer");
+  const int e = elem_bytes(act);
+  if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || !aligned16(conv_state) ||
+      !aligned16(y) || (bias && !aligned16(bias)))
+    return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state and y must be 16-byte aligned");
+  const size_t ny = (size_t)N * C * e;
+  const size_t nx = ((size_t)(N - 1) * xs + C) * e;
+  const size_t ns = (size_t)nseq * 3 * C * 4;
+  if (overlaps(y, ny, x, nx) || overlaps(y, ny, conv_state, ns) || overlaps(y, ny, w, (size_t)C * 16))
+    return fail(GDN_ERR_ALIAS, "y must not overlap x, w or conv_state");
+  if (overlaps(conv_state, ns, x, nx)) return fail(GDN_ERR_ALIAS, "conv_state must not overlap x");
+  return launched(gdn::launch_conv(x, xs, act, w, bias, conv_state, has_init, cu, chunks, nchunks, C,
+                                   write_state, y, as_stream(stream)),
+                  "causal_conv");
+}
+
+int gdn_postconv_l2(const void* y, int64_t ys, int in, int N, int Hk, int Hv, int dk, int dv,
+                    float eps, void* q, void* k, void* v, int out, void* stream) {
+  if (!valid_dtype(in) || !valid_dtype(out)) return fail(GDN_ERR_DTYPE, "unsupported dtype");
+  int st = check_heads(Hk, Hv, dk, dv);
+  if (st != GDN_OK) return st;
+  const int C = 2 * Hk * dk + Hv * dv;
+  if (N < 0 || ys < C) return fail(GDN_ERR_SHAPE, "need N >= 0 and y_row_stride >= C");
+  if (!(eps > 0.f)) return fail(GDN_ERR_SHAPE, "eps must be > 0");
+  if (N == 0) return GDN_OK;
+  if (!y || !q || !k || !v) return fail(GDN_ERR_NULL, "missing required pointer");
+  const int ei = elem_bytes(in), eo = elem_bytes(out);
+  if (!aligned16(y) || ((size_t)ys * ei) % 16 != 0 || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(GDN_ERR_ALIGN, "y rows, q, k and v must be 16-byte aligned");
+  const size_t ny = ((size_t)(N - 1) * ys + C) * ei;
+  const size_t nq = (size_t)N * Hk * dk * eo, nv = (size_t)N * Hv * dv * eo;
+  if (overlaps(q, nq, y, ny) || overlaps(k, nq, y, ny) || overlaps(v, nv, y, ny) ||
+      overlaps(q, nq, k, nq) || overlaps(q, nq, v, nv) || overlaps(k, nq, v, nv))
+    return fail(GDN_ERR_ALIAS, "q, k, v must not overlap y or each other");
+  return launched(gdn::launch_postconv(y, ys, in, N, Hk, Hv, eps, q, k, v, out, as_stream(stream)),
+                  "postconv_l2");
+}
+
+int gdn_delta_rule_prefill(const void* q, const void* k, const void* v, int act, const float* g,
+                           const float* beta, const int32_t* cu, int nseq, int N, int Hk, int Hv,
+                           int dk, int dv, float* state, const uint8_t* has_init, void* o,
+                           void* stream) {
+  int st = check_recurrence(q, k, v, act, g, beta, cu, nseq, N, Hk, Hv, dk, dv, state, o);
+  if (st != GDN_OK || nseq == 0) return st;
+  return launched(gdn::launch_prefill(q, k, v, act, g, beta, cu, nseq, Hk, Hv, state, has_init, o,
+                                      as_stream(stream)),
+                  "delta_rule_prefill");
+}
+
+int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act, const float* g,
+                        const float* beta, const int32_t* cu, int nseq, int N, int Hk, int Hv,
+                        int dk, int dv, float* state, const uint8_t* has_init, void* o,
+                        int commit_state, void* stream) {
+  int st = check_recurrence(q, k, v, act, g, beta, cu, nseq, N, Hk, Hv, dk, dv, state, o);
+  if (st != GDN_OK || nseq == 0 || N == 0) return st;
+  return launched(gdn::launch_step(q, k, v, act, g, beta, cu, nseq, Hk, Hv, state, has_init, o,
+                                   commit_state, as_stream(stream)),
+                  "delta_rule_step");
+}
+
+int gdn_commit(const gdn_layer_io* layers, int L, const int32_t* cu, const int32_t* n_keep,
+               const uint8_t* has_init, int nseq, int C, int Hk, int Hv, int dk, int dv, int act,
+               void* stream) {
+  if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
+  int st = check_heads(Hk, Hv, dk, dv);
+  if (st != GDN_OK) return st;
+  if (L < 0 || nseq < 0) return fail(GDN_ERR_SHAPE, "negative L or nseq");
+  if (C != 2 * Hk * dk + Hv * dv) return fail(GDN_ERR_SHAPE, "C must equal 2*Hk*dk + Hv*dv");
+  if (L == 0 || nseq == 0) return GDN_OK;
+  if (!layers || !cu || !n_keep) return fail(GDN_ERR_NULL, "layers, cu_seqlens and n_keep are required");
+  const long long blocks = (long long)L * nseq * (Hv + (C + 2047) / 2048);
+  if (blocks > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "too many (layer, sequence) pairs");
+  return launched(gdn::launch_commit(layers, L, cu, n_keep, has_init, nseq, C, Hk, Hv, act,
+                                     as_stream(stream)),
+                  "commit");
+}
+
+}  // extern "C"

@@ -1,0 +1,226 @@
+// Exact token chunks and the width-4 depthwise causal conv (gfx950).
+//
+// Conv semantics ("perf(gdn): optimize post-conv and causal-conv kernels",
+// "Blocker": c channels, k = 4 taps; "New issue #305": the first chunk of a
+// sequence reads the stored conv rows, the final rows come from the last
+// tokens):  y[t][c] = bias[c] + sum_j w[c][j] * xe[t-3+j][c], where xe is the
+// sequence input preceded by its 3 stored rows (oldest first).
+//
+// Layout: one workgroup per (chunk, group of 2048 channels); each lane owns
+// 8 adjacent channels, so every token row is read and written with 16-byte
+// accesses, and walks the chunk's tokens in order keeping its 3-token window
+// in registers (no cross-lane traffic, no LDS).  A chunk that is not its
+// sequence's first reads its 3-row halo from x.
+//
+// conv_state ownership: only the FIRST chunk's workgroup touches a
+// sequence's conv_state.  Its lanes read the stored rows, use them for the
+// outputs t < 3 (which forces the loads to complete), and afterwards store
+// the final rows, taken from the last 3 tokens of x (or from the shifted
+// stored rows when the sequence has fewer than 3 tokens).  Each element is
+// read and then written by the same lane, in program order, so updating
+// conv_state in place cannot race with any other workgroup.  This replaces
+// the "last chunk writes" arrangement whose cross-block race the issue
+// describes.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvChannelsPerLane = 8;
+constexpr int kConvChannelsPerBlock = kConvThreads * kConvChannelsPerLane;  // 2048
+constexpr int kConvUnroll = 8;
+
+// ------------------------------------------------------------ chunk builder
+// One workgroup: sequences are scanned 256 at a time; thread i of a round
+// counts the chunks of its sequence, an exclusive scan gives each sequence
+// its first slot, and the thread writes its descriptors.  Slots past the
+// total are marked unused (seq = -1).
+__global__ __launch_bounds__(256) void make_chunks_kernel(const int32_t* __restrict__ cu, int nseq,
+                                                          int chunk_len, gdn_chunk* __restrict__ out,
+                                                          int cap) {
+  __shared__ int s_count[256];
+  __shared__ int s_base;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < nseq; s0 += 256) {
+    const int s = s0 + tid;
+    int begin = 0, len = 0, n = 0;
+    if (s < nseq) {
+      begin = cu[s];
+      len = cu[s + 1] - begin;
+      n = len > 0 ? (len + chunk_len - 1) / chunk_len : 0;
+    }
+    s_count[tid] = n;
+    __syncthreads();
+    // inclusive Hillis-Steele scan over 256 counts
+    for (int off = 1; off < 256; off <<= 1) {
+      int add = tid >= off ? s_count[tid - off] : 0;
+      __syncthreads();
+      s_count[tid] += add;
+      __syncthreads();
+    }
+    const int base = s_base;
+    const int first = base + s_count[tid] - n;
+    for (int j = 0; j < n; ++j) {
+      const int slot = first + j;
+      if (slot < cap) {
+        gdn_chunk c;
+        c.seq = s;
+        c.begin = begin + j * chunk_len;
+        c.end = min(c.begin + chunk_len, begin + len);
+        c.flags = (j == 0 ? GDN_CHUNK_FIRST : 0) | (j == n - 1 ? GDN_CHUNK_LAST : 0);
+        out[slot] = c;
+      }
+    }
+    __syncthreads();
+    if (tid == 255) s_base = base + s_count[255];
+    __syncthreads();
+  }
+  const int total = s_base;
+  for (int slot = total + tid; slot < cap; slot += 256) {
+    gdn_chunk c;
+    c.seq = -1; c.begin = 0; c.end = 0; c.flags = 0;
+    out[slot] = c;
+  }
+}
+
+// ---------------------------------------------------------------- the conv
+template <class T>
+__global__ __launch_bounds__(kConvThreads) void conv_kernel(
+    const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
+    float* conv_state, const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu,
+    const gdn_chunk* __restrict__ chunks, int C, int write_state, T* __restrict__ y) {
+  const gdn_chunk ch = chunks[blockIdx.x];
+  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * kConvChannelsPerLane;
+  if (ch.seq < 0 || c0 >= C) return;
+  const int s = ch.seq;
+  const bool first = (ch.flags & GDN_CHUNK_FIRST) != 0;
+
+  float w0[8], w1[8], w2[8], w3[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 wv = *reinterpret_cast<const float4*>(w + (int64_t)(c0 + i) * 4);
+    w0[i] = wv.x; w1[i] = wv.y; w2[i] = wv.z; w3[i] = wv.w;
+    b[i] = 0.f;
+  }
+  if (bias != nullptr) {
+    const float4 b0 = *reinterpret_cast<const float4*>(bias + c0);
+    const float4 b1 = *reinterpret_cast<const float4*>(bias + c0 + 4);
+    b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
+    b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+  }
+
+  // window: h0 = xe[t-3], h1 = xe[t-2], h2 = xe[t-1]
+  float h0[8], h1[8], h2[8];
+  float* st = conv_state + ((int64_t)s * 3) * C + c0;
+  if (first) {
+    const bool init = has_init == nullptr || has_init[s] != 0;
+    if (init) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 4) {
+        float4 a = *reinterpret_cast<const float4*>(st + i);
+        float4 bb = *reinterpret_cast<const float4*>(st + C + i);
+        float4 c = *reinterpret_cast<const float4*>(st + 2 * C + i);
+        h0[i] = a.x; h0[i + 1] = a.y; h0[i + 2] = a.z; h0[i + 3] = a.w;
+        h1[i] = bb.x; h1[i + 1] = bb.y; h1[i + 2] = bb.z; h1[i + 3] = bb.w;
+        h2[i] = c.x; h2[i + 1] = c.y; h2[i + 2] = c.z; h2[i + 3] = c.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { h0[i] = 0.f; h1[i] = 0.f; h2[i] = 0.f; }
+    }
+  } else {
+    Act<T>::load8(x + (int64_t)(ch.begin - 3) * xs + c0, h0);
+    Act<T>::load8(x + (int64_t)(ch.begin - 2) * xs + c0, h1);
+    Act<T>::load8(x + (int64_t)(ch.begin - 1) * xs + c0, h2);
+  }
+  // the stored rows, kept for sequences shorter than 3 tokens
+  float i0[8], i1[8], i2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { i0[i] = h0[i]; i1[i] = h1[i]; i2[i] = h2[i]; }
+
+  for (int t0 = ch.begin; t0 < ch.end; t0 += kConvUnroll) {
+    float xv[kConvUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kConvUnroll; ++u)
+      if (t0 + u < ch.end) Act<T>::load8(x + (int64_t)(t0 + u) * xs + c0, xv[u]);
+#pragma unroll
+    for (int u = 0; u < kConvUnroll; ++u) {
+      if (t0 + u < ch.end) {
+        float out[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float acc = b[i];
+          acc = __builtin_fmaf(w0[i], h0[i], acc);
+          acc = __builtin_fmaf(w1[i], h1[i], acc);
+          acc = __builtin_fmaf(w2[i], h2[i], acc);
+          acc = __builtin_fmaf(w3[i], xv[u][i], acc);
+          out[i] = acc;
+          h0[i] = h1[i]; h1[i] = h2[i]; h2[i] = xv[u][i];
+        }
+        Act<T>::store8(y + (int64_t)(t0 + u) * C + c0, out);
+      }
+    }
+  }
+
+  if (first && write_state) {
+    const int bos = cu[s], eos = cu[s + 1];
+    const int len = eos - bos;
+    // final rows r = 0..2 are xe[len-3+r]: x when that index is >= 0, else the
+    // stored row 3 + (len-3+r).
+    float r0[8], r1[8], r2[8];
+    if (len >= 3) {
+      Act<T>::load8(x + (int64_t)(eos - 3) * xs + c0, r0);
+      Act<T>::load8(x + (int64_t)(eos - 2) * xs + c0, r1);
+      Act<T>::load8(x + (int64_t)(eos - 1) * xs + c0, r2);
+    } else if (len == 2) {
+      float a[8], bb[8];
+      Act<T>::load8(x + (int64_t)bos * xs + c0, a);
+      Act<T>::load8(x + (int64_t)(bos + 1) * xs + c0, bb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { r0[i] = i2[i]; r1[i] = a[i]; r2[i] = bb[i]; }
+    } else {  // len == 1 (a first chunk is never empty)
+      float a[8];
+      Act<T>::load8(x + (int64_t)bos * xs + c0, a);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { r0[i] = i1[i]; r1[i] = i2[i]; r2[i] = a[i]; }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += 4) {
+      *reinterpret_cast<float4*>(st + i) = make_float4(r0[i], r0[i + 1], r0[i + 2], r0[i + 3]);
+      *reinterpret_cast<float4*>(st + C + i) = make_float4(r1[i], r1[i + 1], r1[i + 2], r1[i + 3]);
+      *reinterpret_cast<float4*>(st + 2 * C + i) = make_float4(r2[i], r2[i + 1], r2[i + 2], r2[i + 3]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out, int cap,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(make_chunks_kernel, dim3(1), dim3(256), 0, st, cu, nseq, chunk_len, out, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                       float* conv_state, const uint8_t* has_init, const int32_t* cu,
+                       const gdn_chunk* chunks, int nchunks, int C, int write_state, void* y,
+                       hipStream_t st) {
+  dim3 grid(nchunks, (C + kConvChannelsPerBlock - 1) / kConvChannelsPerBlock);
+  if (act == GDN_F32) {
+    hipLaunchKernelGGL(conv_kernel<float>, grid, dim3(kConvThreads), 0, st,
+                       static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks,
+                       C, write_state, static_cast<float*>(y));
+  } else {
+    hipLaunchKernelGGL(conv_kernel<uint16_t>, grid, dim3(kConvThreads), 0, st,
+                       static_cast<const uint16_t*>(x), xs, w, bias, conv_state, has_init, cu,
+                       chunks, C, write_state, static_cast<uint16_t*>(y));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,91 @@
+// Device helpers shared by the GDN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bfloat16
+// bfloat16 is stored as its 16 raw bits (uint16_t).
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Activation storage traits: load / store 8 consecutive elements as float.
+template <class T> struct Act;
+
+template <> struct Act<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static void load8(const float* p, float (&v)[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void store8(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+template <> struct Act<uint16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static void load8(const uint16_t* p, float (&v)[8]) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    v[0] = bf16_to_f32(u.x & 0xffffu); v[1] = bf16_to_f32(u.x >> 16);
+    v[2] = bf16_to_f32(u.y & 0xffffu); v[3] = bf16_to_f32(u.y >> 16);
+    v[4] = bf16_to_f32(u.z & 0xffffu); v[5] = bf16_to_f32(u.z >> 16);
+    v[6] = bf16_to_f32(u.w & 0xffffu); v[7] = bf16_to_f32(u.w >> 16);
+  }
+  __device__ __forceinline__ static void store8(uint16_t* p, const float (&v)[8]) {
+    uint4 u;
+    u.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    u.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    u.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+    u.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+    *reinterpret_cast<uint4*>(p) = u;
+  }
+  __device__ __forceinline__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store1(uint16_t* p, float v) {
+    *p = static_cast<uint16_t>(f32_to_bf16(v));
+  }
+};
+
+// ------------------------------------------------------- wave64 DPP moves
+// Row-local (16-lane) data movement.  quad_perm xor-1 = 0xB1, xor-2 = 0x4E,
+// row_half_mirror = 0x141 (lane i <- 7-i within 8), row_mirror = 0x140
+// (lane i <- 15-i within 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 16 lanes of a DPP row, result in every lane of the row.
+// Order: lanes are combined neighbours first, xor 1, 2, 4, 8.  After each
+// level all lanes of a group hold the same value, so the mirror moves used
+// for the 4- and 8-lane levels fetch exactly the partner group's sum, and
+// a + b == b + a keeps the lanes bit-identical.
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_mov<0xB1>(v);
+  v = v + dpp_mov<0x4E>(v);
+  v = v + dpp_mov<0x141>(v);
+  v = v + dpp_mov<0x140>(v);
+  return v;
+}
+
+}  // namespace gdn

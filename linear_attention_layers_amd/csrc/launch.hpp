@@ -1,0 +1,37 @@
+// Host-side launchers of the GDN kernels (internal to libgdn.so).  Arguments
+// are validated by api.cpp before these are called; each returns the HIP
+// status of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+hipError_t launch_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out,
+                              int cap, hipStream_t st);
+
+hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                       float* conv_state, const uint8_t* has_init, const int32_t* cu,
+                       const gdn_chunk* chunks, int nchunks, int C, int write_state, void* y,
+                       hipStream_t st);
+
+hipError_t launch_postconv(const void* y, int64_t ys, int in, int N, int Hk, int Hv, float eps,
+                           void* q, void* k, void* v, int out, hipStream_t st);
+
+hipError_t launch_step(const void* q, const void* k, const void* v, int act, const float* g,
+                       const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
+                       float* state, const uint8_t* has_init, void* o, int commit_state,
+                       hipStream_t st);
+
+hipError_t launch_commit(const gdn_layer_io* layers, int L, const int32_t* cu,
+                         const int32_t* n_keep, const uint8_t* has_init, int nseq, int C,
+                         int Hk, int Hv, int act, hipStream_t st);
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, int act, const float* g,
+                          const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
+                          float* state, const uint8_t* has_init, void* o, hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,271 @@
+"""Thin ctypes binding over libgdn.so (C ABI in include/gdn.h).
+
+Each function here has the name of the C entry point it calls, turns torch
+tensors into pointers, sizes and dtype codes, passes torch's current HIP
+stream, and raises GdnError on a non-OK status.  No step of the computation
+runs in Python: every one is a HIP kernel inside the library.  Importing
+this module fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m linear_attention_layers_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+GDN_F32 = 0
+GDN_BF16 = 1
+CHUNK_LEN = 64
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+
+class gdn_chunk(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("begin", ctypes.c_int32),
+                ("end", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class gdn_layer_io(ctypes.Structure):
+    _fields_ = [("x", _vp), ("x_row_stride", _i64), ("conv_state", _vp), ("state", _vp),
+                ("k", _vp), ("v", _vp), ("g", _vp), ("beta", _vp)]
+
+
+def _sig(name, args, res=_i32):
+    fn = getattr(_lib, name)
+    fn.argtypes = args
+    fn.restype = res
+    return fn
+
+
+_abi_version = _sig("gdn_abi_version", [])
+_status_string = _sig("gdn_status_string", [_i32], ctypes.c_char_p)
+_last_error = _sig("gdn_last_error", [], ctypes.c_char_p)
+_chunk_capacity = _sig("gdn_chunk_capacity", [_i32, _i32, _i32])
+_make_chunks = _sig("gdn_make_chunks", [_vp, _i32, _i32, _vp, _i32])
+_make_chunks_device = _sig("gdn_make_chunks_device", [_vp, _i32, _i32, _vp, _i32, _vp])
+_conv = _sig("gdn_causal_conv_fwd", [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                     _i32, _i32, _i32, _vp, _vp])
+_postconv = _sig("gdn_postconv_l2", [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                                     _vp, _vp, _i32, _vp])
+_prefill = _sig("gdn_delta_rule_prefill", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, _vp, _vp, _vp, _vp])
+_step = _sig("gdn_delta_rule_step", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                     _i32, _i32, _vp, _vp, _vp, _i32, _vp])
+_commit = _sig("gdn_commit", [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                              _vp])
+
+EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
+            "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd",
+            "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_delta_rule_step", "gdn_commit"]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_status_string(status).decode()} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GdnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _code(dtype) -> int:
+    if dtype == torch.float32:
+        return GDN_F32
+    if dtype == torch.bfloat16:
+        return GDN_BF16
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _torch_dtype(code: int):
+    return torch.float32 if code == GDN_F32 else torch.bfloat16
+
+
+def _stream(stream) -> _vp:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream)
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dense(t: torch.Tensor, name: str):
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------- info
+
+def gdn_abi_version() -> int:
+    return int(_abi_version())
+
+
+def gdn_status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def gdn_last_error() -> str:
+    return _last_error().decode(errors="replace")
+
+
+# ---------------------------------------------------------------- chunks
+
+def gdn_chunk_capacity(N: int, nseq: int, chunk_len: int = CHUNK_LEN) -> int:
+    return int(_chunk_capacity(N, nseq, chunk_len))
+
+
+def gdn_make_chunks(cu_seqlens: Sequence[int], chunk_len: int = CHUNK_LEN) -> torch.Tensor:
+    """Host chunk list: returns an int32 CPU tensor [n, 4] = (seq, begin, end, flags)."""
+    cu = torch.as_tensor(list(int(c) for c in cu_seqlens), dtype=torch.int32)
+    nseq = cu.numel() - 1
+    cap = max(gdn_chunk_capacity(int(cu[-1]), nseq, chunk_len), 1)
+    out = torch.empty(cap, 4, dtype=torch.int32)
+    n = int(_make_chunks(_ptr(cu), nseq, chunk_len, _ptr(out), cap))
+    if n < 0:
+        raise GdnError(-n, "gdn_make_chunks")
+    return out[:n].clone()
+
+
+def gdn_make_chunks_device(cu_seqlens: torch.Tensor, N: int, chunk_len: int = CHUNK_LEN,
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Device chunk list with gdn_chunk_capacity slots (unused slots seq = -1)."""
+    _require(cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32, "cu_seqlens: int32 device tensor")
+    nseq = cu_seqlens.numel() - 1
+    cap = gdn_chunk_capacity(N, nseq, chunk_len)
+    if out is None:
+        out = torch.empty(max(cap, 1), 4, dtype=torch.int32, device=cu_seqlens.device)
+    _require(out.shape[0] >= cap and out.dtype == torch.int32 and out.is_contiguous(), "out too small")
+    st = int(_make_chunks_device(_ptr(cu_seqlens), nseq, chunk_len, _ptr(out), cap, _stream(stream)))
+    if st != 0:
+        raise GdnError(-st, "gdn_make_chunks_device")
+    return out[:cap]
+
+
+# ---------------------------------------------------------------- conv
+
+def gdn_causal_conv_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor],
+                        conv_state: torch.Tensor, has_initial_state: Optional[torch.Tensor],
+                        cu_seqlens: torch.Tensor, chunks: torch.Tensor, write_state: bool,
+                        y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    N, C = x.shape
+    _require(x.stride(1) == 1, "x rows must be contiguous")
+    nseq = cu_seqlens.numel() - 1
+    if y is None:
+        y = torch.empty(N, C, dtype=x.dtype, device=x.device)
+    _dense(y, "y")
+    _dense(w, "w")
+    _dense(conv_state, "conv_state")
+    _require(w.dtype == torch.float32 and conv_state.dtype == torch.float32, "w, conv_state: float32")
+    _require(bias is None or bias.dtype == torch.float32, "bias: float32")
+    _require(y.dtype == x.dtype, "y dtype must match x")
+    _check(_conv(_ptr(x), x.stride(0), _code(x.dtype), _ptr(w), _ptr(bias), _ptr(conv_state),
+                 _ptr(has_initial_state), _ptr(cu_seqlens), _ptr(chunks), chunks.shape[0], nseq,
+                 N, C, int(bool(write_state)), _ptr(y), _stream(stream)), "gdn_causal_conv_fwd")
+    return y
+
+
+# ---------------------------------------------------------------- post-conv
+
+def gdn_postconv_l2(y: torch.Tensor, Hk: int, Hv: int, eps: float = 1e-6,
+                    out_dtype=None, q: Optional[torch.Tensor] = None,
+                    k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                    dk: int = 128, dv: int = 128, stream=None):
+    N = y.shape[0]
+    _require(y.stride(1) == 1, "y rows must be contiguous")
+    out_dtype = y.dtype if out_dtype is None else out_dtype
+    dev = y.device
+    if q is None:
+        q = torch.empty(N, Hk, dk, dtype=out_dtype, device=dev)
+    if k is None:
+        k = torch.empty(N, Hk, dk, dtype=out_dtype, device=dev)
+    if v is None:
+        v = torch.empty(N, Hv, dv, dtype=out_dtype, device=dev)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _dense(t, nm)
+        _require(t.dtype == out_dtype, f"{nm} dtype")
+    _check(_postconv(_ptr(y), y.stride(0), _code(y.dtype), N, Hk, Hv, dk, dv, float(eps),
+                     _ptr(q), _ptr(k), _ptr(v), _code(out_dtype), _stream(stream)),
+           "gdn_postconv_l2")
+    return q, k, v
+
+
+# ---------------------------------------------------------------- recurrence
+
+def _recurrence_args(q, k, v, g, beta, cu_seqlens, state, o):
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (state, "state")):
+        _dense(t, nm)
+    _require(k.shape == q.shape and v.shape[0] == N, "q, k, v shapes")
+    _require(g.dtype == torch.float32 and beta.dtype == torch.float32 and state.dtype == torch.float32,
+             "g, beta, state: float32")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v dtypes must match")
+    if o is None:
+        o = torch.empty(N, Hv, dv, dtype=q.dtype, device=q.device)
+    _dense(o, "o")
+    nseq = cu_seqlens.numel() - 1
+    return N, Hk, Hv, dk, dv, nseq, o
+
+
+def gdn_delta_rule_prefill(q, k, v, g, beta, cu_seqlens, state, has_initial_state=None,
+                           o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    N, Hk, Hv, dk, dv, nseq, o = _recurrence_args(q, k, v, g, beta, cu_seqlens, state, o)
+    _check(_prefill(_ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(g), _ptr(beta),
+                    _ptr(cu_seqlens), nseq, N, Hk, Hv, dk, dv, _ptr(state),
+                    _ptr(has_initial_state), _ptr(o), _stream(stream)), "gdn_delta_rule_prefill")
+    return o
+
+
+def gdn_delta_rule_step(q, k, v, g, beta, cu_seqlens, state, has_initial_state=None,
+                        o: Optional[torch.Tensor] = None, commit_state: bool = True,
+                        stream=None) -> torch.Tensor:
+    N, Hk, Hv, dk, dv, nseq, o = _recurrence_args(q, k, v, g, beta, cu_seqlens, state, o)
+    _check(_step(_ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                 nseq, N, Hk, Hv, dk, dv, _ptr(state), _ptr(has_initial_state), _ptr(o),
+                 int(bool(commit_state)), _stream(stream)), "gdn_delta_rule_step")
+    return o
+
+
+# ---------------------------------------------------------------- commit
+
+def gdn_layer_table(layers: List[dict], device) -> torch.Tensor:
+    """Pack per-layer tensors {x, conv_state, state, k, v, g, beta} into a
+    device array of gdn_layer_io (kept alive by the caller)."""
+    arr = (gdn_layer_io * len(layers))()
+    for i, L in enumerate(layers):
+        x = L["x"]
+        _require(x.stride(1) == 1, "x rows must be contiguous")
+        arr[i] = gdn_layer_io(x.data_ptr(), x.stride(0), L["conv_state"].data_ptr(),
+                              L["state"].data_ptr(), L["k"].data_ptr(), L["v"].data_ptr(),
+                              L["g"].data_ptr(), L["beta"].data_ptr())
+    raw = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return raw.to(device)
+
+
+def gdn_commit(layer_table: torch.Tensor, L: int, cu_seqlens: torch.Tensor, n_keep: torch.Tensor,
+               has_initial_state: Optional[torch.Tensor], C: int, Hk: int, Hv: int, act_dtype,
+               dk: int = 128, dv: int = 128, stream=None):
+    _require(layer_table.numel() >= L * ctypes.sizeof(gdn_layer_io), "layer table too small")
+    nseq = cu_seqlens.numel() - 1
+    _check(_commit(_ptr(layer_table), L, _ptr(cu_seqlens), _ptr(n_keep), _ptr(has_initial_state),
+                   nseq, C, Hk, Hv, dk, dv, _code(act_dtype), _stream(stream)), "gdn_commit")

@@ -1,0 +1,182 @@
+"""CPU-side checks of the C ABI: the library loads and exports every entry
+point include/gdn.h declares; the host chunk builder is bit-exact against the
+oracle; argument validation returns the documented status codes before any
+launch (no GPU is touched: every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import gdn_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "linear_attention_layers_amd", "libgdn.so")
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+if not os.path.exists(LIB):
+    pytest.skip("libgdn.so not built (run __graft_entry__.build())", allow_module_level=True)
+
+lib = ctypes.CDLL(LIB)
+vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, LAUNCH, CAPACITY = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for required in ("gdn_causal_conv_fwd", "gdn_postconv_l2", "gdn_delta_rule_prefill",
+                     "gdn_delta_rule_step", "gdn_commit", "gdn_make_chunks"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_names_match_the_abi():
+    # the Python binding is not imported here (it needs torch's HIP stream at
+    # call time, not at import); its list of names must equal the header's
+    src = open(os.path.join(ROOT, "linear_attention_layers_amd", "gdn.py")).read()
+    exported = re.search(r"EXPORTED = \[(.*?)\]", src, re.S).group(1)
+    assert sorted(re.findall(r'"(gdn_[a-z0-9_]+)"', exported)) == declared_functions()
+
+
+def test_abi_version_and_status_strings():
+    lib.gdn_abi_version.restype = i32
+    assert lib.gdn_abi_version() == 1
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [i32]
+    assert lib.gdn_status_string(0) == b"ok"
+    assert lib.gdn_status_string(ALIAS) == b"overlapping buffers"
+
+
+def _make_chunks(cu, chunk_len=64, cap=None):
+    cu = np.asarray(cu, dtype=np.int32)
+    nseq = len(cu) - 1
+    lib.gdn_chunk_capacity.restype = i32
+    lib.gdn_chunk_capacity.argtypes = [i32, i32, i32]
+    bound = lib.gdn_chunk_capacity(int(cu[-1]), nseq, chunk_len)
+    cap = bound if cap is None else cap
+    out = np.zeros((max(cap, 1), 4), dtype=np.int32)
+    lib.gdn_make_chunks.restype = i32
+    lib.gdn_make_chunks.argtypes = [vp, i32, i32, vp, i32]
+    n = lib.gdn_make_chunks(cu.ctypes.data, nseq, chunk_len, out.ctypes.data, cap)
+    return n, out, bound
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_host_make_chunks_bit_exact_and_capacity_is_a_bound(seed):
+    r = np.random.default_rng(seed)
+    lengths = r.integers(0, 400, int(r.integers(1, 40)))
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    M = int(r.choice([3, 16, 64, 100]))
+    n, out, bound = _make_chunks(cu, M)
+    ref = O.make_chunks(cu, M)
+    assert n == len(ref) <= bound
+    assert np.array_equal(out[:n], ref)
+
+
+def test_host_make_chunks_errors():
+    n, _, _ = _make_chunks([0, 200], 64, cap=3)
+    assert n == -CAPACITY
+    n, _, _ = _make_chunks([0, 5, 3], 64)
+    assert n == -SHAPE
+    n, _, _ = _make_chunks([1, 5], 64)
+    assert n == -SHAPE
+    lib.gdn_make_chunks.argtypes = [vp, i32, i32, vp, i32]
+    assert lib.gdn_make_chunks(None, 1, 64, None, 4) == -NULL
+
+
+FAKE = 0x10000000          # 16-byte aligned dummy address; never dereferenced
+
+
+def _postconv(y, ys, N, Hk, Hv, dk, dv, eps, q, k, v, din=1, dout=1):
+    fn = lib.gdn_postconv_l2
+    fn.restype = i32
+    fn.argtypes = [vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, i32, vp]
+    return fn(y, ys, din, N, Hk, Hv, dk, dv, eps, q, k, v, dout, None)
+
+
+def test_postconv_validation():
+    C = 2 * 2 * 128 + 4 * 128
+    base = dict(y=FAKE, ys=C, N=4, Hk=2, Hv=4, dk=128, dv=128, eps=1e-6,
+                q=FAKE + (1 << 24), k=FAKE + (2 << 24), v=FAKE + (3 << 24))
+    assert _postconv(**dict(base, dk=64)) == SHAPE
+    assert _postconv(**dict(base, Hv=3)) == SHAPE
+    assert _postconv(**dict(base, eps=0.0)) == SHAPE
+    assert _postconv(**dict(base, ys=C - 8)) == SHAPE
+    assert _postconv(**dict(base, y=None)) == NULL
+    assert _postconv(**dict(base, q=FAKE + 8)) == ALIGN
+    assert _postconv(**dict(base, q=FAKE + 64)) == ALIAS          # q inside y
+    assert _postconv(**dict(base), din=7) == DTYPE
+    assert _postconv(**dict(base, N=0)) == OK                      # empty: no launch
+
+
+def test_conv_validation():
+    fn = lib.gdn_causal_conv_fwd
+    fn.restype = i32
+    fn.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    C = 1024
+    args = [FAKE, C, 1, FAKE + (1 << 24), None, FAKE + (2 << 24), None, FAKE + (3 << 24),
+            FAKE + (4 << 24), 4, 2, 100, C, 1, FAKE + (5 << 24), None]
+
+    def call(**kw):
+        a = list(args)
+        idx = {"x": 0, "xs": 1, "act": 2, "C": 12, "y": 14, "w": 3, "N": 11}
+        for k_, v_ in kw.items():
+            a[idx[k_]] = v_
+        return fn(*a)
+
+    assert call(C=1020) == SHAPE
+    assert call(xs=C - 8) == SHAPE
+    assert call(act=5) == DTYPE
+    assert call(w=None) == NULL
+    assert call(x=FAKE + 2) == ALIGN
+    assert call(y=FAKE + 1024) == ALIAS
+    assert call(N=0) == OK
+
+
+def test_recurrence_validation():
+    fn = lib.gdn_delta_rule_prefill
+    fn.restype = i32
+    fn.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    base = [FAKE, FAKE + (1 << 24), FAKE + (2 << 24), 1, FAKE + (3 << 24), FAKE + (4 << 24),
+            FAKE + (5 << 24), 2, 100, 2, 4, 128, 128, FAKE + (6 << 24), None, FAKE + (7 << 24), None]
+
+    def call(**kw):
+        a = list(base)
+        idx = {"q": 0, "act": 3, "cu": 6, "Hk": 9, "Hv": 10, "dk": 11, "state": 13, "o": 15}
+        for k_, v_ in kw.items():
+            a[idx[k_]] = v_
+        return fn(*a)
+
+    assert call(Hv=3) == SHAPE
+    assert call(dk=64) == SHAPE
+    assert call(act=2) == DTYPE
+    assert call(cu=None) == NULL
+    assert call(o=FAKE + 4) == ALIGN
+    assert call(o=FAKE + 256) == ALIAS      # o inside q
+    step = lib.gdn_delta_rule_step
+    step.restype = i32
+    step.argtypes = fn.argtypes[:-1] + [i32, vp]
+    a = list(base)
+    a[9] = 3
+    assert step(*(a[:-1] + [1, None])) == SHAPE
+
+
+def test_commit_validation():
+    fn = lib.gdn_commit
+    fn.restype = i32
+    fn.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    assert fn(FAKE, 2, FAKE, FAKE, None, 4, 1000, 2, 4, 128, 128, 1, None) == SHAPE
+    assert fn(None, 2, FAKE, FAKE, None, 4, 1024, 2, 4, 128, 128, 1, None) == NULL
+    assert fn(FAKE, 0, FAKE, FAKE, None, 4, 1024, 2, 4, 128, 128, 1, None) == OK

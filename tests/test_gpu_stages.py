@@ -1,0 +1,381 @@
+"""Stage-by-stage parity of the HIP library against the CPU oracle, at sizes
+the oracle finishes in seconds, spanning several tiles / chunks with ragged
+tails, plus the edge cases of each stage.  Every call goes through the C ABI
+(the ctypes binding).  Stage isolation: each oracle stage consumes the GPU's
+own output of the previous stage."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_testlib as TL
+from oracle import gdn_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+gdn = pytest.importorskip("linear_attention_layers_amd.gdn")
+from linear_attention_layers_amd import inputs as I  # noqa: E402
+
+DEV = "cuda"
+
+
+def _cu(lengths):
+    return I.cu_from_lengths(lengths)
+
+
+# ---------------------------------------------------------------- chunks
+
+@pytest.mark.parametrize("lengths", [[1], [64], [65], [0, 5, 0, 130, 3], [2048] * 3 + [1] * 5,
+                                     list(range(0, 300, 7)),
+                                     [int(x) for x in np.random.default_rng(3).integers(0, 150, 700)]])
+def test_make_chunks_device_bit_exact(lengths):
+    cu = _cu(lengths)
+    out = gdn.gdn_make_chunks_device(cu.to(DEV), int(cu[-1]))
+    ref = O.make_chunks(cu.tolist(), 64)
+    got = out.cpu().numpy()
+    assert got.shape[0] == gdn.gdn_chunk_capacity(int(cu[-1]), len(lengths))
+    assert np.array_equal(got[:len(ref)], ref)
+    assert np.all(got[len(ref):, 0] == -1)
+    host = gdn.gdn_make_chunks(cu.tolist()).numpy()
+    assert np.array_equal(host, ref)
+
+
+# ---------------------------------------------------------------- conv
+
+CONV_CASES = [
+    # act, geometry, lengths, has_init, bias_std, row_pad
+    ("f32", I.GEO_TINY, [64], [1], 0.0, 0),
+    ("bf16", I.GEO_TINY, [1, 2, 3, 63, 64, 65, 129, 200], [1, 0, 1, 0, 1, 1, 0, 1], 0.3, 0),
+    ("f32", I.Geometry(Hk=1, Hv=1), [5, 70, 2, 1], [0, 1, 1, 1], 0.5, 8),
+    ("bf16", I.Geometry(Hk=5, Hv=15), [130, 7, 64], [1, 1, 0], 0.0, 16),
+]
+
+
+def _conv_ref(lb, conv_state_in, write_state):
+    x = TL.np64(lb.x)
+    hi = lb.has_init.numpy()
+    cu = lb.cu_seqlens.tolist()
+    b = None if lb.conv_b is None else TL.np64(lb.conv_b)
+    y, st = O.causal_conv(x, TL.np64(lb.conv_w), b, TL.np64(conv_state_in), hi, cu, write_state)
+    scale = TL.conv_scale(x, TL.np64(lb.conv_w), b, TL.np64(conv_state_in), hi, cu)
+    return y, st, scale
+
+
+@pytest.mark.parametrize("case", range(len(CONV_CASES)))
+@pytest.mark.parametrize("write_state", [True, False])
+def test_conv_parity(case, write_state):
+    act, geo, lengths, hinit, bias_std, pad = CONV_CASES[case]
+    lb = I.make_layer(geo, lengths, act, 100 + case, bias_std=bias_std, has_init=hinit,
+                      x_row_pad=pad)
+    # poison the stored rows of sequences without initial state
+    cs0 = lb.conv_state.clone()
+    for s, h in enumerate(hinit):
+        if not h:
+            cs0[s] = float("nan")
+    cs = cs0.to(DEV)
+    xd = lb.x.to(DEV) if pad == 0 else _padded_to_device(lb)
+    cu = lb.cu_seqlens.to(DEV)
+    chunks = gdn.gdn_make_chunks_device(cu, lb.N)
+    y = gdn.gdn_causal_conv_fwd(xd, lb.conv_w.to(DEV), TL.dev(lb.conv_b), cs,
+                                lb.has_init.to(DEV), cu, chunks, write_state)
+    torch.cuda.synchronize()
+    y_ref, st_ref, scale = _conv_ref(lb, cs0, write_state)
+    assert np.all(np.isfinite(TL.np64(y)))
+    TL.check_conv(TL.np64(y), y_ref, scale, act)
+    got_st = cs.cpu().numpy().astype(np.float64)
+    if write_state:
+        assert np.array_equal(got_st, st_ref)          # exact copies of inputs
+    else:
+        assert np.array_equal(np.isnan(got_st), np.isnan(cs0.numpy()))
+        assert np.array_equal(np.nan_to_num(got_st), np.nan_to_num(cs0.numpy().astype(np.float64)))
+
+
+def _padded_to_device(lb):
+    """Re-create the padded row storage on the device (stride > C)."""
+    N, C = lb.x.shape
+    stride = lb.x.stride(0)
+    full = torch.zeros(N, stride, dtype=lb.x.dtype)
+    full[:, :C] = lb.x
+    return full.to(DEV)[:, :C]
+
+
+def test_conv_delta_kernel_is_an_exact_shift():
+    geo = I.Geometry(Hk=1, Hv=1)
+    lb = I.make_layer(geo, [3, 1, 70], "bf16", 7)
+    C = geo.C
+    for shift in range(4):
+        w = torch.zeros(C, 4)
+        w[:, 3 - shift] = 1.0
+        cs = lb.conv_state.to(DEV)
+        cu = lb.cu_seqlens.to(DEV)
+        y = gdn.gdn_causal_conv_fwd(lb.x.to(DEV), w.to(DEV), None, cs, None, cu,
+                                    gdn.gdn_make_chunks_device(cu, lb.N), False)
+        y_ref, _ = O.causal_conv(TL.np64(lb.x), w.numpy(), None, TL.np64(lb.conv_state), [1, 1, 1],
+                                 lb.cu_seqlens.tolist(), False)
+        assert np.array_equal(TL.np64(y), O.round_to_bf16(y_ref))
+
+
+@pytest.mark.parametrize("order", ["reversed", "shuffled"])
+def test_conv_state_in_place_is_race_free(order):
+    """Sequences longer than one chunk with initial state, in place, with the
+    chunk list reordered: every repetition must match the oracle exactly."""
+    lb = I.make_layer(I.GEO_TINY, [200, 65, 64, 300, 5], "bf16", 11)
+    host = gdn.gdn_make_chunks(lb.cu_seqlens.tolist())
+    idx = torch.arange(host.shape[0] - 1, -1, -1) if order == "reversed" else \
+        torch.randperm(host.shape[0], generator=torch.Generator().manual_seed(5))
+    chunks = host[idx].contiguous().to(DEV)
+    cu = lb.cu_seqlens.to(DEV)
+    x = lb.x.to(DEV)
+    w = lb.conv_w.to(DEV)
+    y_ref, st_ref, scale = _conv_ref(lb, lb.conv_state, True)
+    y_first = None
+    for rep in range(100):
+        cs = lb.conv_state.to(DEV)
+        y = gdn.gdn_causal_conv_fwd(x, w, None, cs, None, cu, chunks, True)
+        got = cs.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, st_ref), f"repetition {rep}"
+        if y_first is None:
+            y_first = y.clone()
+            TL.check_conv(TL.np64(y), y_ref, scale, "bf16")
+        else:
+            assert torch.equal(y, y_first)
+
+
+def test_conv_two_calls_equal_one():
+    lb = I.make_layer(I.GEO_TINY, [150], "bf16", 12)
+    cu_all = lb.cu_seqlens.to(DEV)
+    w = lb.conv_w.to(DEV)
+    cs_a = lb.conv_state.to(DEV)
+    y_all = gdn.gdn_causal_conv_fwd(lb.x.to(DEV), w, None, cs_a, None, cu_all,
+                                    gdn.gdn_make_chunks_device(cu_all, 150), True)
+    for split in (1, 2, 3, 64, 100):
+        cs_b = lb.conv_state.to(DEV)
+        parts = []
+        for (a, b) in ((0, split), (split, 150)):
+            cu = torch.tensor([0, b - a], dtype=torch.int32, device=DEV)
+            parts.append(gdn.gdn_causal_conv_fwd(lb.x[a:b].contiguous().to(DEV), w, None, cs_b, None,
+                                                 cu, gdn.gdn_make_chunks_device(cu, b - a), True))
+        assert torch.equal(torch.cat(parts), y_all)
+        assert torch.equal(cs_b, cs_a)
+
+
+# ---------------------------------------------------------------- post-conv
+
+def _y(geo, N, act, scale=2.0, seed=0, lo=None, hi=None):
+    g = torch.Generator().manual_seed(seed)
+    if lo is not None:
+        y = lo + (hi - lo) * torch.rand(N, geo.C, generator=g)
+    else:
+        y = torch.randn(N, geo.C, generator=g) * scale
+    return y.to(TL.ACT[act])
+
+
+@pytest.mark.parametrize("act_in", ["f32", "bf16"])
+def test_postconv_f32_arm_matches_documented_order(act_in):
+    geo = I.Geometry(Hk=3, Hv=6)
+    y = _y(geo, 300, act_in, seed=1)
+    q, k, v = gdn.gdn_postconv_l2(y.to(DEV), geo.Hk, geo.Hv, 1e-6, out_dtype=torch.float32)
+    qr, kr, vr = O.postconv_l2_f32_tree(TL.np64(y), geo.Hk, geo.Hv, 128, 128, 1e-6)
+    for got, ref in ((q, qr), (k, kr)):
+        d = TL.ulp_dist_f32(got.cpu().numpy(), ref)
+        assert d.max() <= TL.L2_ULP_F32, f"max ulp {d.max()}"
+    s_ref = O.silu(TL.np64(y))[:, 2 * geo.Hk * 128:].reshape(300, geo.Hv, 128)
+    np.testing.assert_allclose(v.cpu().numpy(), s_ref, rtol=TL.SILU_REL_F32, atol=0)
+    assert np.array_equal(v.cpu().numpy(), vr)
+
+
+def test_postconv_silu_identity_region_pins_the_order_exactly():
+    """y in [20, 40]: SiLU(y) == y in float32, so q_hat depends only on the
+    summation order; it must equal the oracle's documented order bit for bit."""
+    geo = I.Geometry(Hk=4, Hv=4)
+    y = _y(geo, 2000, "f32", seed=2, lo=20.0, hi=40.0)
+    q, k, v = gdn.gdn_postconv_l2(y.to(DEV), geo.Hk, geo.Hv, 1e-6, out_dtype=torch.float32)
+    qr, kr, vr = O.postconv_l2_f32_tree(TL.np64(y), geo.Hk, geo.Hv, 128, 128, 1e-6)
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(k.cpu().numpy(), kr)
+    assert np.array_equal(v.cpu().numpy(), y[:, 8 * 128:].reshape(2000, 4, 128).numpy())
+
+
+@pytest.mark.parametrize("act_in", ["f32", "bf16"])
+def test_postconv_bf16_output_within_one_step(act_in):
+    geo = I.GEO_8192
+    y = _y(geo, 96, act_in, seed=3)
+    q, k, v = gdn.gdn_postconv_l2(y.to(DEV), geo.Hk, geo.Hv, 1e-6, out_dtype=torch.bfloat16)
+    qr, kr, vr = O.postconv_l2(TL.np64(y), geo.Hk, geo.Hv, 128, 128, np.float64(np.float32(1e-6)))
+    for got, ref in ((q, qr), (k, kr), (v, vr)):
+        d = TL.ulp_dist_bf16(got.float().cpu().numpy(), O.round_to_bf16(ref).astype(np.float32))
+        assert d.max() <= TL.L2_ULP_BF16
+
+
+def test_postconv_closed_forms_and_zero_head():
+    geo = I.Geometry(Hk=2, Hv=2)
+    y = _y(geo, 40, "f32", seed=4)
+    y[3, :128] = -1e4                     # SiLU = -0 on a whole q head
+    eps = 1e-3
+    q, k, v = gdn.gdn_postconv_l2(y.to(DEV), geo.Hk, geo.Hv, eps, out_dtype=torch.float32)
+    s = O.silu(TL.np64(y))
+    sq, sk, _ = O.split_heads(s, geo.Hk, geo.Hv, 128, 128)
+    for got, raw in ((q, sq), (k, sk)):
+        sig = np.sum(raw ** 2, axis=-1)
+        np.testing.assert_allclose(np.linalg.norm(got.cpu().numpy().astype(np.float64), axis=-1),
+                                   np.sqrt(sig / (sig + eps)), rtol=2e-6)
+    assert np.all(q[3, 0].cpu().numpy() == 0)
+
+
+# ---------------------------------------------------------------- recurrence
+
+def _rec_inputs(act, geo, lengths, has_init, seed, state_std=0.3, gate="softplus"):
+    """Run conv + post-conv on the GPU and return the recurrence inputs."""
+    lb = I.make_layer(geo, lengths, act, seed, state_std=state_std, has_init=has_init, gate=gate)
+    out = TL.gpu_layer(lb)
+    return lb, out
+
+
+def _rec_ref(lb, out, state_in=None):
+    hi = lb.has_init.numpy()
+    st = TL.np64(lb.state if state_in is None else state_in)
+    return O.delta_rule_recurrent(TL.np64(out["q"]), TL.np64(out["k"]), TL.np64(out["v"]),
+                                  TL.np64(lb.g), TL.np64(lb.beta), st, hi,
+                                  lb.cu_seqlens.tolist(), lb.geo.Hk, lb.geo.Hv)
+
+
+REC_CASES = [
+    ("f32", I.GEO_TINY, [64], [1]),
+    ("f32", I.GEO_TINY, [1, 2, 3, 63, 65, 129], [1, 0, 1, 1, 0, 1]),
+    ("bf16", I.GEO_TINY, [1, 2, 3, 63, 64, 65, 129, 200], [1, 0, 1, 0, 1, 1, 0, 1]),
+    ("bf16", I.Geometry(Hk=1, Hv=3), [130, 7], [1, 0]),
+    ("bf16", I.Geometry(Hk=2, Hv=2), [300], [1]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(REC_CASES)))
+def test_prefill_parity(case):
+    act, geo, lengths, hinit = REC_CASES[case]
+    lb, out = _rec_inputs(act, geo, lengths, hinit, 200 + case)
+    torch.cuda.synchronize()
+    o_ref, st_ref = _rec_ref(lb, out)
+    tol = TL.REC_F32 if act == "f32" else TL.REC_BF16
+    TL.check_normwise(TL.np64(out["o"]), o_ref, tol, axes=(2,), what="o")
+    TL.check_normwise(TL.np64(out["state"]), st_ref, tol, axes=(2, 3), what="state")
+
+
+def test_prefill_ignores_poisoned_state_without_init():
+    geo = I.GEO_TINY
+    lb = I.make_layer(geo, [70, 5], "bf16", 300, state_std=0.3, has_init=[0, 0])
+    lb.state[:] = float("nan")
+    out = TL.gpu_layer(lb)
+    assert torch.isfinite(out["o"].float()).all() and torch.isfinite(out["state"]).all()
+
+
+def _step_run(act, geo, lengths, hinit, seed, commit):
+    lb = I.make_layer(geo, lengths, act, seed, state_std=0.3, has_init=hinit)
+    cu = lb.cu_seqlens.to(DEV)
+    hi = lb.has_init.to(DEV)
+    cs = lb.conv_state.to(DEV)
+    y = gdn.gdn_causal_conv_fwd(lb.x.to(DEV), lb.conv_w.to(DEV), None, cs, hi, cu,
+                                gdn.gdn_make_chunks_device(cu, lb.N), commit)
+    q, k, v = gdn.gdn_postconv_l2(y, geo.Hk, geo.Hv, 1e-6)
+    st = lb.state.to(DEV)
+    g, beta = lb.g.to(DEV), lb.beta.to(DEV)
+    o = gdn.gdn_delta_rule_step(q, k, v, g, beta, cu, st, hi, commit_state=commit)
+    return lb, dict(q=q, k=k, v=v, o=o, state=st, g=g, beta=beta, cu=cu, hi=hi, x=lb.x.to(DEV),
+                    conv_state=cs)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("commit", [True, False])
+def test_step_parity(act, commit):
+    geo = I.GEO_TINY
+    lengths = [1, 2, 5, 8, 3, 1]
+    hinit = [1, 1, 0, 1, 1, 0]
+    lb, out = _step_run(act, geo, lengths, hinit, 400, commit)
+    torch.cuda.synchronize()
+    o_ref, st_ref = _rec_ref(lb, out)
+    tol = TL.REC_F32 if act == "f32" else TL.REC_BF16
+    TL.check_normwise(TL.np64(out["o"]), o_ref, tol, axes=(2,), what="o")
+    if commit:
+        TL.check_normwise(TL.np64(out["state"]), st_ref, tol, axes=(2, 3), what="state")
+    else:
+        assert torch.equal(out["state"].cpu(), lb.state)
+
+
+def test_step_multi_token_equals_single_token_steps():
+    geo = I.GEO_TINY
+    lengths = [1, 4, 8, 2]
+    lb, out = _step_run("bf16", geo, lengths, [1, 1, 1, 0], 500, True)
+    cu = lb.cu_seqlens.tolist()
+    for s in range(len(lengths)):
+        st = lb.state[s:s + 1].to(DEV).contiguous()
+        for t in range(cu[s], cu[s + 1]):
+            sl = slice(t, t + 1)
+            init = torch.tensor([1 if (t > cu[s] or lb.has_init[s]) else 0], dtype=torch.uint8,
+                                device=DEV)
+            one = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+            o1 = gdn.gdn_delta_rule_step(out["q"][sl].contiguous(), out["k"][sl].contiguous(),
+                                         out["v"][sl].contiguous(), out["g"][sl].contiguous(),
+                                         out["beta"][sl].contiguous(), one, st, init,
+                                         commit_state=True)
+            assert torch.equal(o1, out["o"][sl]), f"seq {s} token {t}"
+        assert torch.equal(st[0], out["state"][s]), f"seq {s} state"
+
+
+def test_prefill_and_step_agree_within_tolerance():
+    """The chunked and the per-token forms are both correct: not bitwise equal,
+    but within the recurrence bound of each other."""
+    geo = I.GEO_TINY
+    lb = I.make_layer(geo, [1, 8, 64, 100], "bf16", 600, state_std=0.3)
+    out = TL.gpu_layer(lb)
+    st2 = lb.state.to(DEV)
+    o2 = gdn.gdn_delta_rule_step(out["q"], out["k"], out["v"], out["g"], out["beta"], out["cu"],
+                                 st2, out["hi"], commit_state=True)
+    TL.check_normwise(TL.np64(out["o"]), TL.np64(o2), TL.REC_BF16, axes=(2,), what="o")
+    TL.check_normwise(TL.np64(out["state"]), TL.np64(st2), TL.REC_BF16, axes=(2, 3), what="state")
+
+
+# ---------------------------------------------------------------- commit
+
+def test_commit_parity_and_bitwise_equal_to_step_commit():
+    geo = I.GEO_TINY
+    L = 3
+    lengths = [1, 8, 5, 3, 7, 2]
+    n_keep = [0, 8, 2, 3, 0, 1]
+    hinit = [1, 1, 1, 0, 1, 1]
+    layers, runs = [], []
+    for layer in range(L):
+        lb, out = _step_run("bf16", geo, lengths, hinit, 700 + 10 * layer, False)
+        runs.append((lb, out))
+        layers.append(dict(x=out["x"], conv_state=out["conv_state"], state=out["state"],
+                           k=out["k"], v=out["v"], g=out["g"], beta=out["beta"]))
+    table = gdn.gdn_layer_table(layers, DEV)
+    nk = torch.tensor(n_keep, dtype=torch.int32, device=DEV)
+    cu = runs[0][1]["cu"]
+    hi = runs[0][1]["hi"]
+    gdn.gdn_commit(table, L, cu, nk, hi, geo.C, geo.Hk, geo.Hv, torch.bfloat16)
+    torch.cuda.synchronize()
+    # the kept tokens, packed, for the reference forward with commit
+    keep_idx = torch.cat([torch.arange(c, c + n) for c, n in zip(lb.cu_seqlens[:-1].tolist(), n_keep)])
+    cu_keep = I.cu_from_lengths(n_keep).to(DEV)
+    for layer, (lb, out) in enumerate(runs):
+        # oracle
+        cs_ref, st_ref = O.commit(TL.np64(lb.x), TL.np64(lb.conv_state), TL.np64(lb.state),
+                                  TL.np64(out["k"]), TL.np64(out["v"]), TL.np64(lb.g),
+                                  TL.np64(lb.beta), lb.has_init.numpy(), lb.cu_seqlens.tolist(),
+                                  n_keep, geo.Hk, geo.Hv)
+        assert np.array_equal(out["conv_state"].cpu().numpy().astype(np.float64), cs_ref)
+        TL.check_normwise(TL.np64(out["state"]), st_ref, TL.REC_BF16, axes=(2, 3), what="state")
+        # n = 0 leaves the state untouched bit for bit
+        for s, n in enumerate(n_keep):
+            if n == 0:
+                assert torch.equal(out["state"][s].cpu(), lb.state[s])
+                assert torch.equal(out["conv_state"][s].cpu(), lb.conv_state[s])
+        # bitwise equal to a committing step / conv over the kept tokens
+        kd = keep_idx.to(DEV)
+        st2 = lb.state.to(DEV)
+        gdn.gdn_delta_rule_step(out["q"][kd].contiguous(), out["k"][kd].contiguous(),
+                                out["v"][kd].contiguous(), out["g"][kd].contiguous(),
+                                out["beta"][kd].contiguous(), cu_keep, st2, hi, commit_state=True)
+        cs2 = lb.conv_state.to(DEV)
+        xk = out["x"][kd].contiguous()
+        gdn.gdn_causal_conv_fwd(xk, lb.conv_w.to(DEV), None, cs2, hi, cu_keep,
+                                gdn.gdn_make_chunks_device(cu_keep, int(sum(n_keep))), True)
+        assert torch.equal(st2, out["state"]), f"layer {layer}"
+        assert torch.equal(cs2, out["conv_state"]), f"layer {layer}"

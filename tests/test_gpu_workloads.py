@@ -1,0 +1,228 @@
+"""Parity at the five workloads' full sizes, run the way the benchmark
+launches them (one conv, one post-conv and one recurrence launch per layer).
+Outputs the oracle cannot afford in full are sampled: a subset of v-heads
+(with their k-head) for the recurrence, token windows for the conv and the
+post-conv, a subset of layers for deep stacks.  Integer work and state
+copies are checked bit for bit everywhere."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_testlib as TL
+from oracle import gdn_oracle as O
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+gdn = pytest.importorskip("linear_attention_layers_amd.gdn")
+from linear_attention_layers_amd import inputs as I  # noqa: E402
+
+DEV = "cuda"
+
+
+def _head_subset(lb, out, heads):
+    """Recurrence inputs restricted to the v-heads `heads` (all sharing one
+    k-head) so the oracle can run them alone."""
+    ratio = lb.geo.Hv // lb.geo.Hk
+    kh = heads[0] // ratio
+    assert all(h // ratio == kh for h in heads)
+    q = TL.np64(out["q"][:, kh:kh + 1])
+    k = TL.np64(out["k"][:, kh:kh + 1])
+    v = TL.np64(out["v"][:, heads])
+    g = TL.np64(lb.g[:, heads])
+    b = TL.np64(lb.beta[:, heads])
+    st = TL.np64(lb.state[:, heads])
+    return q, k, v, g, b, st
+
+
+def _check_recurrence(lb, out, heads, tol, state_in=None):
+    q, k, v, g, b, st = _head_subset(lb, out, heads)
+    if state_in is not None:
+        st = state_in
+    o_ref, st_ref = O.delta_rule_recurrent(q, k, v, g, b, st, lb.has_init.numpy(),
+                                           lb.cu_seqlens.tolist(), 1, len(heads))
+    TL.check_normwise(TL.np64(out["o"][:, heads]), o_ref, tol, axes=(2,), what=f"o heads {heads}")
+    TL.check_normwise(TL.np64(out["state"][:, heads]), st_ref, tol, axes=(2, 3),
+                      what=f"state heads {heads}")
+
+
+def _check_conv_windows(lb, out, windows):
+    """Conv outputs on token windows [a, b) inside one sequence, computed by
+    the oracle from the 3 tokens before a (zero stored rows suffice because
+    every output in the window only reaches 3 tokens back)."""
+    x = TL.np64(lb.x)
+    w = TL.np64(lb.conv_w)
+    for a, b in windows:
+        a0 = a - 3
+        xs = x[a0:b]
+        y_ref, _ = O.causal_conv(xs, w, None, np.zeros((1, 3, x.shape[1])), [0], [0, b - a0], False)
+        scale = TL.conv_scale(xs, w, None, np.zeros((1, 3, x.shape[1])), [0], [0, b - a0])
+        TL.check_conv(TL.np64(out["y"][a:b]), y_ref[3:], scale[3:], lb.act, what=f"conv [{a},{b})")
+
+
+def _check_conv_heads(lb, out):
+    """The first 3 tokens of every sequence (they read the stored rows) and
+    the final conv_state (bit-exact)."""
+    cu = lb.cu_seqlens.tolist()
+    hi = lb.has_init.numpy()
+    x = TL.np64(lb.x)
+    w = TL.np64(lb.conv_w)
+    cs = TL.np64(lb.conv_state)
+    idx = [t for s in range(lb.nseq) for t in range(cu[s], min(cu[s] + 3, cu[s + 1]))]
+    sub_len = [min(3, cu[s + 1] - cu[s]) for s in range(lb.nseq)]
+    sub_cu = I.cu_from_lengths(sub_len).tolist()
+    y_ref, _ = O.causal_conv(x[idx], w, None, cs, hi, sub_cu, False)
+    scale = TL.conv_scale(x[idx], w, None, cs, hi, sub_cu)
+    TL.check_conv(TL.np64(out["y"][idx]), y_ref, scale, lb.act, what="conv heads")
+    # final rows: the last three of [stored ; x]
+    for s in range(lb.nseq):
+        L = cu[s + 1] - cu[s]
+        old = cs[s] if hi[s] else np.zeros_like(cs[s])
+        ext = np.concatenate([old, x[cu[s]:cu[s + 1]][-3:]])[-3:]
+        assert np.array_equal(TL.np64(out["conv_state"][s]), ext), f"conv_state seq {s} (L={L})"
+
+
+def _check_postconv_tokens(lb, out, tokens, eps=1e-6):
+    y = TL.np64(out["y"][tokens])
+    qr, kr, vr = O.postconv_l2(y, lb.geo.Hk, lb.geo.Hv, 128, 128, np.float64(np.float32(eps)))
+    if lb.act == "bf16":
+        for got, ref in ((out["q"], qr), (out["k"], kr), (out["v"], vr)):
+            d = TL.ulp_dist_bf16(got[tokens].float().cpu().numpy(), O.round_to_bf16(ref).astype(np.float32))
+            assert d.max() <= TL.L2_ULP_BF16
+    else:
+        qf, kf, vf = O.postconv_l2_f32_tree(y, lb.geo.Hk, lb.geo.Hv, 128, 128, eps)
+        for got, ref in ((out["q"], qf), (out["k"], kf)):
+            assert TL.ulp_dist_f32(got[tokens].cpu().numpy(), ref).max() <= TL.L2_ULP_F32
+        np.testing.assert_allclose(TL.np64(out["v"][tokens]), vr, rtol=TL.SILU_REL_F32, atol=0)
+
+
+# --------------------------------------------------------------------------
+
+def test_tiny_f32_layer_all_outputs():
+    lb = I.tiny_f32()
+    out = TL.gpu_layer(lb)
+    torch.cuda.synchronize()
+    cu = lb.cu_seqlens.tolist()
+    x, w, cs, hi = TL.np64(lb.x), TL.np64(lb.conv_w), TL.np64(lb.conv_state), lb.has_init.numpy()
+    y_ref, cs_ref = O.causal_conv(x, w, None, cs, hi, cu, True)
+    TL.check_conv(TL.np64(out["y"]), y_ref, TL.conv_scale(x, w, None, cs, hi, cu), "f32")
+    assert np.array_equal(TL.np64(out["conv_state"]), cs_ref)
+    _check_postconv_tokens(lb, out, list(range(64)))
+    _check_recurrence(lb, out, [0, 1], TL.REC_F32)
+    _check_recurrence(lb, out, [2, 3], TL.REC_F32)
+    # whole chain from the raw inputs, rounding only at the storage points
+    qr, kr, vr = O.postconv_l2_f32_tree(O.round_to(y_ref, "f32"), 2, 4, 128, 128, 1e-6)
+    o_ref, st_ref = O.delta_rule_recurrent(qr, kr, vr, TL.np64(lb.g), TL.np64(lb.beta),
+                                           TL.np64(lb.state), hi, cu, 2, 4)
+    TL.check_normwise(TL.np64(out["o"]), o_ref, TL.REC_F32, axes=(2,), what="chain o")
+    TL.check_normwise(TL.np64(out["state"]), st_ref, TL.REC_F32, axes=(2, 3), what="chain state")
+
+
+def test_varlen_prefill_bf16_full_size():
+    lb = I.varlen_prefill()
+    out = TL.gpu_layer(lb)
+    torch.cuda.synchronize()
+    cu = lb.cu_seqlens.tolist()
+    _check_conv_heads(lb, out)
+    wins = [(cu[s] + 3, cu[s] + 3 + 70) for s in range(lb.nseq)] + \
+           [(cu[s + 1] - 66, cu[s + 1]) for s in range(lb.nseq)]
+    _check_conv_windows(lb, out, wins)
+    toks = list(range(0, lb.N, 37))
+    _check_postconv_tokens(lb, out, toks)
+    for heads in ([0, 1], [14, 15], [30, 31]):
+        _check_recurrence(lb, out, heads, TL.REC_BF16)
+
+
+def test_long_prefill_32k_sampled():
+    lb = I.long_prefill()
+    out = TL.gpu_layer(lb)
+    torch.cuda.synchronize()
+    _check_conv_heads(lb, out)
+    _check_conv_windows(lb, out, [(3, 200), (16000, 16130), (32768 - 130, 32768)])
+    _check_postconv_tokens(lb, out, list(range(0, lb.N, 997)))
+    _check_recurrence(lb, out, [0, 1], TL.REC_BF16)
+    _check_recurrence(lb, out, [31], TL.REC_BF16)
+
+
+def test_spec_verify_36_layers_then_one_commit():
+    L = 36
+    layers, runs = [], []
+    lengths, n_keep = I.spec_verify_window()
+    for layer in range(L):
+        lb = I.spec_verify_layer(layer)
+        cu = lb.cu_seqlens.to(DEV)
+        cs = lb.conv_state.to(DEV)
+        x = lb.x.to(DEV)
+        y = gdn.gdn_causal_conv_fwd(x, lb.conv_w.to(DEV), None, cs, None, cu,
+                                    gdn.gdn_make_chunks_device(cu, lb.N), False)
+        q, k, v = gdn.gdn_postconv_l2(y, lb.geo.Hk, lb.geo.Hv, 1e-6)
+        st = lb.state.to(DEV)
+        g, beta = lb.g.to(DEV), lb.beta.to(DEV)
+        o = gdn.gdn_delta_rule_step(q, k, v, g, beta, cu, st, None, commit_state=False)
+        out = dict(y=y, q=q, k=k, v=v, o=o, state=st, conv_state=cs, g=g, beta=beta, x=x)
+        if layer in (0, 35):
+            torch.cuda.synchronize()
+            xs, ws, css = TL.np64(lb.x), TL.np64(lb.conv_w), TL.np64(lb.conv_state)
+            hi1 = np.ones(lb.nseq)
+            cu_l = lb.cu_seqlens.tolist()
+            y_ref, _ = O.causal_conv(xs, ws, None, css, hi1, cu_l, False)
+            TL.check_conv(TL.np64(y), y_ref, TL.conv_scale(xs, ws, None, css, hi1, cu_l), "bf16")
+            _check_postconv_tokens(lb, out, list(range(lb.N)))
+            for heads in ([0, 1], [30, 31]):
+                q_, k_, v_, g_, b_, st_ = _head_subset(lb, out, heads)
+                o_ref, _ = O.delta_rule_recurrent(q_, k_, v_, g_, b_, st_, hi1, cu_l, 1, len(heads))
+                TL.check_normwise(TL.np64(o[:, heads]), o_ref, TL.REC_BF16, axes=(2,), what="verify o")
+            assert torch.equal(st.cpu(), lb.state) and torch.equal(cs.cpu(), lb.conv_state)
+        runs.append((lb, out))
+        layers.append(dict(x=x, conv_state=cs, state=st, k=k, v=v, g=g, beta=beta))
+    table = gdn.gdn_layer_table(layers, DEV)
+    lb0 = runs[0][0]
+    gdn.gdn_commit(table, L, lb0.cu_seqlens.to(DEV), lb0.n_keep.to(DEV), None, lb0.geo.C,
+                   lb0.geo.Hk, lb0.geo.Hv, torch.bfloat16)
+    torch.cuda.synchronize()
+    for layer, (lb, out) in enumerate(runs):
+        cu = lb.cu_seqlens.tolist()
+        # conv rows: exact for every layer
+        x = TL.np64(lb.x)
+        cs = TL.np64(lb.conv_state)
+        for s, n in enumerate(n_keep):
+            ext = np.concatenate([cs[s], x[cu[s]:cu[s] + n]])[-3:]
+            assert np.array_equal(TL.np64(out["conv_state"][s]), ext), f"layer {layer} seq {s}"
+        if layer in (0, 17, 35):
+            for heads in ([0, 1], [22, 23]):
+                q_, k_, v_, g_, b_, st_ = _head_subset(lb, out, heads)
+                _, st_ref = O.commit(x, cs, st_, k_, v_, g_, b_, np.ones(lb.nseq), cu, n_keep, 1,
+                                     len(heads))
+                TL.check_normwise(TL.np64(out["state"][:, heads]), st_ref, TL.REC_BF16, axes=(2, 3),
+                                  what=f"commit layer {layer}")
+
+
+def test_mixed_serving_24_layers_sampled():
+    L = 24
+    for layer in range(L):
+        lb = I.mixed_serving_layer(layer)
+        npre = lb.meta["n_prefill"]
+        cu_h = lb.cu_seqlens
+        Npre = int(cu_h[npre])
+        cu = cu_h.to(DEV)
+        cs = lb.conv_state.to(DEV)
+        y = gdn.gdn_causal_conv_fwd(lb.x.to(DEV), lb.conv_w.to(DEV), None, cs, None, cu,
+                                    gdn.gdn_make_chunks_device(cu, lb.N), True)
+        q, k, v = gdn.gdn_postconv_l2(y, lb.geo.Hk, lb.geo.Hv, 1e-6)
+        st = lb.state.to(DEV)
+        g, beta = lb.g.to(DEV), lb.beta.to(DEV)
+        o = torch.empty_like(v)
+        gdn.gdn_delta_rule_prefill(q[:Npre], k[:Npre], v[:Npre], g[:Npre], beta[:Npre],
+                                   cu[:npre + 1], st[:npre], None, o=o[:Npre])
+        cu_dec = (cu[npre:] - Npre).contiguous()
+        gdn.gdn_delta_rule_step(q[Npre:], k[Npre:], v[Npre:], g[Npre:], beta[Npre:], cu_dec,
+                                st[npre:], None, o=o[Npre:], commit_state=True)
+        if layer in (0, 23):
+            torch.cuda.synchronize()
+            out = dict(y=y, q=q, k=k, v=v, o=o, state=st, conv_state=cs)
+            _check_conv_heads(lb, out)
+            cuh = cu_h.tolist()
+            _check_conv_windows(lb, out, [(cuh[s] + 3, min(cuh[s] + 100, cuh[s + 1]))
+                                          for s in range(npre)])
+            _check_postconv_tokens(lb, out, list(range(0, lb.N, 53)) + list(range(Npre, lb.N)))
+            for heads in ([0], [15]):
+                _check_recurrence(lb, out, heads, TL.REC_BF16)
