@@ -134,10 +134,11 @@ int gdn_make_chunks_device(const int32_t* cu_seqlens, int nseq, int chunk_len,
  * multiplies the current token.
  * When write_state != 0, conv_state[s] becomes the last 3 rows of
  * [stored rows ; x of sequence s]; otherwise conv_state is not written.
- * One workgroup per (chunk, 2048-channel group) owns each sequence's
- * conv_state: the first chunk's workgroup reads the stored rows and, later
- * in the same threads' program order, writes the final rows, so the
- * in-place update has no cross-workgroup race.
+ * Exactly one wave per (sequence, 512-channel group) touches conv_state:
+ * wave 0 of the sequence's first chunk reads the stored rows and, later in
+ * the same lanes' program order, writes the final rows, so the in-place
+ * update has no cross-workgroup race.  Non-first chunks must start at least
+ * 3 tokens into their sequence (true for any chunk_len >= 3).
  *   x           (device) [N][x_row_stride] act, x_row_stride >= C, rows
  *               16-byte aligned
  *   w           (device) float [C][4];  bias (device) float [C] or NULL (0)

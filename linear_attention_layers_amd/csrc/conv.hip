@@ -6,13 +6,13 @@
 // tokens):  y[t][c] = bias[c] + sum_j w[c][j] * xe[t-3+j][c], where xe is the
 // sequence input preceded by its 3 stored rows (oldest first).
 //
-// Layout: one workgroup per (chunk, group of 2048 channels); each lane owns
+// Layout: one workgroup per (chunk, group of 512 channels); each lane owns
 // 8 adjacent channels, so every token row is read and written with 16-byte
-// accesses, and walks the chunk's tokens in order keeping its 3-token window
-// in registers (no cross-lane traffic, no LDS).  A chunk that is not its
-// sequence's first reads its 3-row halo from x.
+// accesses; each of the 4 waves takes 16 of the chunk's tokens and walks them
+// in order keeping the 3-token window in registers (no cross-lane traffic,
+// no LDS).  A wave reads its 3-row halo from x unless it starts a sequence.
 //
-// conv_state ownership: only the FIRST chunk's workgroup touches a
+// conv_state ownership: only wave 0 of the FIRST chunk's workgroup touches a
 // sequence's conv_state.  Its lanes read the stored rows, use them for the
 // outputs t < 3 (which forces the loads to complete), and afterwards store
 // the final rows, taken from the last 3 tokens of x (or from the shifted
@@ -28,10 +28,10 @@ namespace gdn {
 
 namespace {
 
-constexpr int kConvThreads = 256;
+constexpr int kConvThreads = 256;                 // 4 waves
 constexpr int kConvChannelsPerLane = 8;
-constexpr int kConvChannelsPerBlock = kConvThreads * kConvChannelsPerLane;  // 2048
-constexpr int kConvUnroll = 8;
+constexpr int kConvChannelsPerBlock = 64 * kConvChannelsPerLane;   // 512
+constexpr int kConvTokensPerWave = 16;            // 4 waves x 16 = one 64-token chunk
 
 // ------------------------------------------------------------ chunk builder
 // One workgroup: sequences are scanned 256 at a time; thread i of a round
@@ -89,16 +89,57 @@ __global__ __launch_bounds__(256) void make_chunks_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------- the conv
+// Workgroup = (chunk slot, group of 512 channels); wave w handles tokens
+// [16 w, 16 w + 16) of the chunk and lane l channels 8 l .. 8 l + 7 of the
+// group.  A lane issues its 3 halo rows and its 16 token rows up front (19
+// independent 16-byte loads), then computes and stores 16 outputs.  Only
+// wave 0 of a sequence's first chunk touches conv_state (see the file
+// comment).
 template <class T>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
     float* conv_state, const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu,
     const gdn_chunk* __restrict__ chunks, int C, int write_state, T* __restrict__ y) {
   const gdn_chunk ch = chunks[blockIdx.x];
-  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * kConvChannelsPerLane;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c0 = (blockIdx.y * 64 + lane) * kConvChannelsPerLane;
   if (ch.seq < 0 || c0 >= C) return;
   const int s = ch.seq;
-  const bool first = (ch.flags & GDN_CHUNK_FIRST) != 0;
+  const int t_begin = ch.begin + kConvTokensPerWave * wave;
+  const int t_end = min(t_begin + kConvTokensPerWave, ch.end);
+  const bool owner = wave == 0 && (ch.flags & GDN_CHUNK_FIRST) != 0;   // reads and writes conv_state
+  if (t_begin >= t_end && !owner) return;
+
+  // window rows xe[t-3], xe[t-2], xe[t-1] for t = t_begin
+  float h0[8], h1[8], h2[8];
+  float* st = conv_state + ((int64_t)s * 3) * C + c0;
+  const bool init = has_init == nullptr || has_init[s] != 0;
+  if (owner) {
+    if (init) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(st + i);
+        const float4 bb = *reinterpret_cast<const float4*>(st + C + i);
+        const float4 c = *reinterpret_cast<const float4*>(st + 2 * C + i);
+        h0[i] = a.x; h0[i + 1] = a.y; h0[i + 2] = a.z; h0[i + 3] = a.w;
+        h1[i] = bb.x; h1[i + 1] = bb.y; h1[i + 2] = bb.z; h1[i + 3] = bb.w;
+        h2[i] = c.x; h2[i + 1] = c.y; h2[i + 2] = c.z; h2[i + 3] = c.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { h0[i] = 0.f; h1[i] = 0.f; h2[i] = 0.f; }
+    }
+  } else {
+    // the 3 rows before t_begin lie in the same sequence: a non-first chunk
+    // starts at least 64 tokens in, and waves > 0 start 16 w tokens in
+    Act<T>::load8(x + (int64_t)(t_begin - 3) * xs + c0, h0);
+    Act<T>::load8(x + (int64_t)(t_begin - 2) * xs + c0, h1);
+    Act<T>::load8(x + (int64_t)(t_begin - 1) * xs + c0, h2);
+  }
+  // the stored rows, kept for sequences shorter than 3 tokens
+  float i0[8], i1[8], i2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { i0[i] = h0[i]; i1[i] = h1[i]; i2[i] = h2[i]; }
 
   float w0[8], w1[8], w2[8], w3[8], b[8];
 #pragma unroll
@@ -114,60 +155,43 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
   }
 
-  // window: h0 = xe[t-3], h1 = xe[t-2], h2 = xe[t-1]
-  float h0[8], h1[8], h2[8];
-  float* st = conv_state + ((int64_t)s * 3) * C + c0;
-  if (first) {
-    const bool init = has_init == nullptr || has_init[s] != 0;
-    if (init) {
+  // all token rows of this wave, loaded before any use (rows past t_end
+  // re-read row t_begin and are never stored)
+  typename Act<T>::Raw xr[kConvTokensPerWave];
 #pragma unroll
-      for (int i = 0; i < 8; i += 4) {
-        float4 a = *reinterpret_cast<const float4*>(st + i);
-        float4 bb = *reinterpret_cast<const float4*>(st + C + i);
-        float4 c = *reinterpret_cast<const float4*>(st + 2 * C + i);
-        h0[i] = a.x; h0[i + 1] = a.y; h0[i + 2] = a.z; h0[i + 3] = a.w;
-        h1[i] = bb.x; h1[i + 1] = bb.y; h1[i + 2] = bb.z; h1[i + 3] = bb.w;
-        h2[i] = c.x; h2[i + 1] = c.y; h2[i + 2] = c.z; h2[i + 3] = c.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { h0[i] = 0.f; h1[i] = 0.f; h2[i] = 0.f; }
-    }
-  } else {
-    Act<T>::load8(x + (int64_t)(ch.begin - 3) * xs + c0, h0);
-    Act<T>::load8(x + (int64_t)(ch.begin - 2) * xs + c0, h1);
-    Act<T>::load8(x + (int64_t)(ch.begin - 1) * xs + c0, h2);
+  for (int u = 0; u < kConvTokensPerWave; ++u) {
+    const int t = (t_begin + u < t_end) ? t_begin + u : t_begin;
+    xr[u] = Act<T>::load_raw(x + (int64_t)t * xs + c0);
   }
-  // the stored rows, kept for sequences shorter than 3 tokens
-  float i0[8], i1[8], i2[8];
+  float x0[8], x1[8];   // the first two rows, kept for sequences shorter than 3 tokens
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { i0[i] = h0[i]; i1[i] = h1[i]; i2[i] = h2[i]; }
-
-  for (int t0 = ch.begin; t0 < ch.end; t0 += kConvUnroll) {
-    float xv[kConvUnroll][8];
+  for (int u = 0; u < kConvTokensPerWave; ++u) {
+    if (t_begin + u < t_end) {
+      float xv[8], out[8];
+      Act<T>::unpack(xr[u], xv);
 #pragma unroll
-    for (int u = 0; u < kConvUnroll; ++u)
-      if (t0 + u < ch.end) Act<T>::load8(x + (int64_t)(t0 + u) * xs + c0, xv[u]);
-#pragma unroll
-    for (int u = 0; u < kConvUnroll; ++u) {
-      if (t0 + u < ch.end) {
-        float out[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float acc = b[i];
-          acc = __builtin_fmaf(w0[i], h0[i], acc);
-          acc = __builtin_fmaf(w1[i], h1[i], acc);
-          acc = __builtin_fmaf(w2[i], h2[i], acc);
-          acc = __builtin_fmaf(w3[i], xv[u][i], acc);
-          out[i] = acc;
-          h0[i] = h1[i]; h1[i] = h2[i]; h2[i] = xv[u][i];
-        }
-        Act<T>::store8(y + (int64_t)(t0 + u) * C + c0, out);
+      for (int i = 0; i < 8; ++i) {
+        float acc = b[i];
+        acc = __builtin_fmaf(w0[i], h0[i], acc);
+        acc = __builtin_fmaf(w1[i], h1[i], acc);
+        acc = __builtin_fmaf(w2[i], h2[i], acc);
+        acc = __builtin_fmaf(w3[i], xv[i], acc);
+        out[i] = acc;
+        h0[i] = h1[i]; h1[i] = h2[i]; h2[i] = xv[i];
       }
+      if (u == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x0[i] = xv[i];
+      }
+      if (u == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x1[i] = xv[i];
+      }
+      Act<T>::store8(y + (int64_t)(t_begin + u) * C + c0, out);
     }
   }
 
-  if (first && write_state) {
+  if (owner && write_state) {
     const int bos = cu[s], eos = cu[s + 1];
     const int len = eos - bos;
     // final rows r = 0..2 are xe[len-3+r]: x when that index is >= 0, else the
@@ -178,16 +202,11 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(
       Act<T>::load8(x + (int64_t)(eos - 2) * xs + c0, r1);
       Act<T>::load8(x + (int64_t)(eos - 1) * xs + c0, r2);
     } else if (len == 2) {
-      float a[8], bb[8];
-      Act<T>::load8(x + (int64_t)bos * xs + c0, a);
-      Act<T>::load8(x + (int64_t)(bos + 1) * xs + c0, bb);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { r0[i] = i2[i]; r1[i] = a[i]; r2[i] = bb[i]; }
+      for (int i = 0; i < 8; ++i) { r0[i] = i2[i]; r1[i] = x0[i]; r2[i] = x1[i]; }
     } else {  // len == 1 (a first chunk is never empty)
-      float a[8];
-      Act<T>::load8(x + (int64_t)bos * xs + c0, a);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { r0[i] = i1[i]; r1[i] = i2[i]; r2[i] = a[i]; }
+      for (int i = 0; i < 8; ++i) { r0[i] = i1[i]; r1[i] = i2[i]; r2[i] = x0[i]; }
     }
 #pragma unroll
     for (int i = 0; i < 8; i += 4) {

@@ -7,6 +7,8 @@
 namespace gdn {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- bfloat16
@@ -16,12 +18,15 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
 
+// Two floats to packed bf16 (low half = a), round to nearest, ties to even:
+// one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // Round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return pack_bf16x2(f, 0.f) & 0xffffu;
 }
 
 // Activation storage traits: load / store 8 consecutive elements as float.
@@ -29,6 +34,18 @@ template <class T> struct Act;
 
 template <> struct Act<float> {
   static constexpr int kBytes = 4;
+  // 8 elements in storage form
+  struct Raw { float4 a, b; };
+  __device__ __forceinline__ static Raw load_raw(const float* p) {
+    Raw r;
+    r.a = *reinterpret_cast<const float4*>(p);
+    r.b = *reinterpret_cast<const float4*>(p + 4);
+    return r;
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, float (&v)[8]) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  }
   __device__ __forceinline__ static void load8(const float* p, float (&v)[8]) {
     float4 a = *reinterpret_cast<const float4*>(p);
     float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -45,6 +62,18 @@ template <> struct Act<float> {
 
 template <> struct Act<uint16_t> {
   static constexpr int kBytes = 2;
+  struct Raw { uint4 u; };
+  __device__ __forceinline__ static Raw load_raw(const uint16_t* p) {
+    Raw r;
+    r.u = *reinterpret_cast<const uint4*>(p);
+    return r;
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, float (&v)[8]) {
+    v[0] = bf16_to_f32(r.u.x & 0xffffu); v[1] = bf16_to_f32(r.u.x >> 16);
+    v[2] = bf16_to_f32(r.u.y & 0xffffu); v[3] = bf16_to_f32(r.u.y >> 16);
+    v[4] = bf16_to_f32(r.u.z & 0xffffu); v[5] = bf16_to_f32(r.u.z >> 16);
+    v[6] = bf16_to_f32(r.u.w & 0xffffu); v[7] = bf16_to_f32(r.u.w >> 16);
+  }
   __device__ __forceinline__ static void load8(const uint16_t* p, float (&v)[8]) {
     uint4 u = *reinterpret_cast<const uint4*>(p);
     v[0] = bf16_to_f32(u.x & 0xffffu); v[1] = bf16_to_f32(u.x >> 16);
@@ -54,10 +83,10 @@ template <> struct Act<uint16_t> {
   }
   __device__ __forceinline__ static void store8(uint16_t* p, const float (&v)[8]) {
     uint4 u;
-    u.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-    u.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-    u.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
-    u.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = u;
   }
   __device__ __forceinline__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }

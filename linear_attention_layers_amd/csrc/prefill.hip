@@ -7,29 +7,38 @@
 // the chunk-64 WY form derived from the per-token rule.  For a chunk of n
 // tokens (local index i) entering with state S0:
 //   G_i = sum_{m<=i} g_m,  gamma_i = exp(G_i),  d_i = exp(G_{n-1} - G_i)
-//   A_ij = b_i exp(G_i - G_j) (k_i . k_j)  (j < i),   T = (I + A)^-1
-//   Z = K S0^T,   R_i = b_i (v_i - gamma_i Z_i),   U = T R
+//   A_ij = b_i exp(G_i - G_j) (k_i . k_j)  (j < i)
+//   Z = K S0^T,   R_i = b_i (v_i - gamma_i Z_i),   (I + A) U = R
 //   O = diag(gamma) Q S0^T + P U,  P_ij = exp(G_i - G_j) (q_i . k_j) (j <= i)
-//   S = gamma_{n-1} S0 + (U^T diag(d)) K
-// (U = T diag(b) V - T diag(b gamma) K S0^T is the usual WY factor; writing it
-// as T R needs no separate W = T diag(b gamma) K.)
+//   S = gamma_{n-1} S0 + (diag(d) U)^T K
+// (U = T diag(b) V - T diag(b gamma) K S0^T with T = (I + A)^-1 is the usual
+// WY factor; here it is reached by solving (I + A) U = R blockwise.)
 //
-// Work split: rows of S (the dv index) evolve independently, so one
-// workgroup owns one (sequence, v-head, slice of DVS state rows) and walks
-// the sequence's chunks in order, carrying its DVS x 128 float32 slice of S
-// in MFMA accumulator registers.  Per chunk, everything is staged in LDS:
-// K, K^T, Q (bf16 exact), V slice, then K K^T and Q K^T (MFMA), the decay /
-// beta scaling, the unit-lower-triangular inverse (16x16 diagonal blocks by
-// forward substitution in one wave, off-diagonal blocks by block forward
-// substitution), and the state-dependent products Z, Q S0^T, U, O and the
-// state update (MFMA).
+// Work split.  Rows of S (the dv index) evolve independently.  A workgroup
+// owns one (sequence, v-head, slice of 16*NW state rows) and walks the
+// sequence's chunks in order; wave w owns 16 state rows and holds them
+// TRANSPOSED (S^T, 8 tiles of 16x16) in MFMA accumulators.  An accumulator
+// tile holds element [4*(lane/16) + e][lane % 16], which is exactly the
+// B-operand layout of the next product (contraction index = tile row), so
+// the chain Z -> R -> U -> (O, S) passes its operands in registers.  Only K,
+// Q, the triangular factors and P live in LDS, shared by the waves; the
+// K^T operand of the state update is read from K with the transposing LDS
+// load ds_read_b64_tr_b16.
 //
-// Precision: with bf16 activations the contractions run on
-// v_mfma_f32_16x16x32_bf16.  Operands that are bf16 inputs (K, Q) are exact;
-// float32 operands (T, P, R, U, S0) are split into hi + lo bf16 parts and
-// multiplied as hi*hi + hi*lo + lo*hi, i.e. about 16 significant bits per
-// operand with float32 accumulation.  With float32 activations every
-// product uses v_mfma_f32_16x16x4_f32.
+// Per chunk (3 barriers): stage K, Q; then every wave computes Z = K S0^T and
+// Q S0^T for its rows plus its share of the 10 lower 16x16 tile pairs of
+// K K^T and Q K^T (scaled into -A, the diagonal blocks of A, and P), and the
+// waves holding a diagonal pair invert that unit-lower-triangular block in
+// float32; then U_i = T_ii (R_i - sum_{m<i} A_im U_m) block by block, O and
+// the state update.  The next chunk's K, Q, V, g and beta are loaded into
+// registers while the current chunk computes.
+//
+// Precision.  bf16 activations: every contraction is one bf16 MFMA pass
+// (v_mfma_f32_16x16x32_bf16, or 16x16x16 for the 16-wide block solve) with
+// float32 accumulation; the state is carried in float32 accumulators and
+// rounded to bf16 only as an MFMA operand; the 16x16 diagonal inverses are
+// float32.  float32 activations: every contraction uses
+// v_mfma_f32_16x16x4_f32 on float32 operands.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -39,439 +48,529 @@ namespace {
 
 constexpr int BT = 64;    // chunk length
 constexpr int DK = 128;   // head size
-constexpr int NW = 4;     // waves per workgroup
-constexpr int NT = NW * 64;
+constexpr float kLog2e = 1.4426950408889634f;
 
-struct ModeBF16 {
-  using elem = uint16_t;
-  static constexpr int KS = 32;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ------------------------------------------------------------ MFMA operands
+// A 16 x 16 (rows x contraction) fragment: lane (r, kg) = (lane % 16,
+// lane / 16) holds contraction slots 4kg .. 4kg+3 of row r.  A 16 x 32
+// fragment holds slots 4kg..4kg+3 of the first 16 and then of the second 16.
+// Every operand uses this slot order, and an accumulator tile's rows
+// 4kg..4kg+3 are a lane's slots, so tiles feed the B side directly.
+template <class T> struct Prec;
+
+template <> struct Prec<uint16_t> {
+  using E = uint16_t;
   static constexpr int PAD = 8;
-  static constexpr bool kSplit = true;
+  struct F16 { uint2 v; };
+  struct F32 { uint4 v; };
+  // row-major LDS matrix, fragment of rows row0.., contraction kb..
+  __device__ __forceinline__ static F16 lds16(const E* p, int ld, int row, int kb, int kg) {
+    F16 f;
+    f.v = *reinterpret_cast<const uint2*>(p + row * ld + kb + 4 * kg);
+    return f;
+  }
+  __device__ __forceinline__ static F32 lds32(const E* p, int ld, int row, int kb, int kg) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p + row * ld + kb + 4 * kg);
+    const uint2 b = *reinterpret_cast<const uint2*>(p + row * ld + kb + 16 + 4 * kg);
+    F32 f;
+    f.v = make_uint4(a.x, a.y, b.x, b.y);
+    return f;
+  }
+  // Transposed fragment of a row-major LDS matrix M: rows = M's columns
+  // c0..c0+15, contraction = M's rows kb..kb+31.  In each 16-lane group the
+  // transposing load hands lane r, slot j the element loaded by lane
+  // 4j + r/4 at slot r%4, so lane s of group kg loads M[kb + 4kg + s/4]
+  // [c0 + 4 (s%4) .. +3].
+  __device__ __forceinline__ static F32 ldsT32(const E* p, int ld, int c0, int kb, int lane) {
+    const int s = lane & 15, kg = lane >> 4;
+    const E* a = p + (kb + 4 * kg + (s >> 2)) * ld + c0 + 4 * (s & 3);
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 16 * ld));
+    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+    F32 f;
+    f.v = make_uint4(ux.x, ux.y, uy.x, uy.y);
+    return f;
+  }
+  __device__ __forceinline__ static F16 reg16(f32x4 d) {
+    F16 f;
+    f.v = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+    return f;
+  }
+  __device__ __forceinline__ static F32 reg32(f32x4 d0, f32x4 d1) {
+    F32 f;
+    f.v = make_uint4(pack_bf16x2(d0[0], d0[1]), pack_bf16x2(d0[2], d0[3]), pack_bf16x2(d1[0], d1[1]),
+                     pack_bf16x2(d1[2], d1[3]));
+    return f;
+  }
+  __device__ __forceinline__ static f32x4 mma16(F16 a, F16 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v),
+                                                     __builtin_bit_cast(s16x4, b.v), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 mma32(F32 a, F32 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                    __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void put(E* p, float x) { *p = static_cast<E>(f32_to_bf16(x)); }
+  // 8 consecutive activations in storage form (one 16-byte piece)
+  struct Raw8 { uint4 v; };
+  __device__ __forceinline__ static Raw8 load_raw8(const uint16_t* p) {
+    Raw8 r;
+    r.v = *reinterpret_cast<const uint4*>(p);
+    return r;
+  }
+  __device__ __forceinline__ static Raw8 zero_raw8() { Raw8 r; r.v = make_uint4(0, 0, 0, 0); return r; }
+  __device__ __forceinline__ static void store_raw8(E* p, Raw8 r) { *reinterpret_cast<uint4*>(p) = r.v; }
+  __device__ __forceinline__ static float to_f32(E x) { return bf16_to_f32(x); }
 };
-struct ModeF32 {
-  using elem = float;
-  static constexpr int KS = 4;
+
+template <> struct Prec<float> {
+  using E = float;
   static constexpr int PAD = 4;
-  static constexpr bool kSplit = false;
-};
-
-// An LDS matrix operand: element (row i, contraction index k) is at
-// hi[i * rs + k * cs]; lo (bf16 mode only, may be null) holds the residual.
-template <class M> struct Opnd {
-  const typename M::elem* hi;
-  const typename M::elem* lo;
-  int rs, cs;
-};
-
-__device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// acc += A[i0 .. i0+15][k0 .. k1) * B^T[j0 .. j0+15][k0 .. k1)^T.
-// Lane l supplies row (l % 16) of A and of B^T for contraction slice l / 16;
-// the accumulator holds D[4 (l / 16) + e][l % 16] in element e.
-template <class M>
-__device__ __forceinline__ f32x4 mma(f32x4 acc, const Opnd<M>& A, int i0, const Opnd<M>& B, int j0,
-                                     int k0, int k1, int lane) {
-  const int r = lane & 15, kg = lane >> 4;
-  if constexpr (M::kSplit) {
-    for (int kk = k0; kk < k1; kk += 32) {
-      const int off = kk + 8 * kg;
-      const uint4 ah = *reinterpret_cast<const uint4*>(A.hi + (i0 + r) * A.rs + off);
-      const uint4 bh = *reinterpret_cast<const uint4*>(B.hi + (j0 + r) * B.rs + off);
-      if (A.lo != nullptr) {
-        const uint4 al = *reinterpret_cast<const uint4*>(A.lo + (i0 + r) * A.rs + off);
-        acc = mfma_bf16(al, bh, acc);
-      }
-      if (B.lo != nullptr) {
-        const uint4 bl = *reinterpret_cast<const uint4*>(B.lo + (j0 + r) * B.rs + off);
-        acc = mfma_bf16(ah, bl, acc);
-      }
-      acc = mfma_bf16(ah, bh, acc);
+  struct F16 { f32x4 v; };
+  struct F32 { f32x4 a, b; };
+  __device__ __forceinline__ static F16 lds16(const E* p, int ld, int row, int kb, int kg) {
+    F16 f;
+    const float4 t = *reinterpret_cast<const float4*>(p + row * ld + kb + 4 * kg);
+    f.v = f32x4{t.x, t.y, t.z, t.w};
+    return f;
+  }
+  __device__ __forceinline__ static F32 lds32(const E* p, int ld, int row, int kb, int kg) {
+    F32 f;
+    f.a = lds16(p, ld, row, kb, kg).v;
+    f.b = lds16(p, ld, row, kb + 16, kg).v;
+    return f;
+  }
+  __device__ __forceinline__ static F32 ldsT32(const E* p, int ld, int c0, int kb, int lane) {
+    const int r = lane & 15, kg = lane >> 4;
+    F32 f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f.a[t] = p[(kb + 4 * kg + t) * ld + c0 + r];
+      f.b[t] = p[(kb + 16 + 4 * kg + t) * ld + c0 + r];
     }
-  } else {
-    for (int kk = k0; kk < k1; kk += 4) {
-      const float a = A.hi[(i0 + r) * A.rs + (kk + kg) * A.cs];
-      const float b = B.hi[(j0 + r) * B.rs + (kk + kg) * B.cs];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-    }
+    return f;
   }
-  return acc;
-}
-
-// Store a float32 value into an operand matrix (split into hi/lo in bf16 mode).
-template <class M>
-__device__ __forceinline__ void put(typename M::elem* hi, typename M::elem* lo, int idx, float x) {
-  if constexpr (M::kSplit) {
-    const uint32_t h = f32_to_bf16(x);
-    hi[idx] = static_cast<uint16_t>(h);
-    lo[idx] = static_cast<uint16_t>(f32_to_bf16(x - bf16_to_f32(h)));
-  } else {
-    hi[idx] = x;
+  __device__ __forceinline__ static F16 reg16(f32x4 d) { F16 f; f.v = d; return f; }
+  __device__ __forceinline__ static F32 reg32(f32x4 d0, f32x4 d1) { F32 f; f.a = d0; f.b = d1; return f; }
+  // slot t of lane kg is contraction index 4kg + t: four k = 4 steps
+  __device__ __forceinline__ static f32x4 mma4x(f32x4 a, f32x4 b, f32x4 c) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], c, 0, 0, 0);
+    return c;
   }
-}
-
-template <class M>
-__device__ __forceinline__ float get(const typename M::elem* hi, const typename M::elem* lo, int idx) {
-  if constexpr (M::kSplit) {
-    return bf16_to_f32(hi[idx]) + bf16_to_f32(lo[idx]);
-  } else {
-    return hi[idx];
+  __device__ __forceinline__ static f32x4 mma16(F16 a, F16 b, f32x4 c) { return mma4x(a.v, b.v, c); }
+  __device__ __forceinline__ static f32x4 mma32(F32 a, F32 b, f32x4 c) {
+    c = mma4x(a.a, b.a, c);
+    return mma4x(a.b, b.b, c);
   }
-}
-
-template <class M, int DVS> struct __attribute__((aligned(16))) Smem {
-  static constexpr int LDK = DK + M::PAD;   // 128-wide rows
-  static constexpr int LDT = BT + M::PAD;   // 64-wide rows
-  static constexpr int NS = M::kSplit ? 2 : 1;
-  using E = typename M::elem;
-  E K[BT * LDK];                          // K rows (token, feature)
-  E KT[M::kSplit ? DK * LDT : 4];         // K^T (feature, token), bf16 mode only
-  E Q[BT * LDK];
-  E V[BT * DVS];                          // this slice of V (token, row)
-  float A[BT * (BT + 1)];                 // K K^T, then the scaled strict lower part A
-  E T[NS * BT * LDT];                     // (I + A)^-1
-  E P[NS * BT * LDT];                     // masked, decayed Q K^T
-  E RT[NS * DVS * LDT];                   // R^T (row, token)
-  E UT[NS * DVS * LDT];                   // U^T
-  union {
-    E UdT[NS * DVS * LDT];                // U^T diag(d)
-    float X[NW * 16 * 17];                // per-wave scratch of the triangular solve
-  };
-  E S[NS * DVS * LDK];                    // S0 slice (row, feature)
-  float G[BT], Gam[BT], Beta[BT], D[BT];
-  float gamma_last;
+  __device__ __forceinline__ static void put(E* p, float x) { *p = x; }
+  struct Raw8 { float4 a, b; };
+  __device__ __forceinline__ static Raw8 load_raw8(const float* p) {
+    Raw8 r;
+    r.a = *reinterpret_cast<const float4*>(p);
+    r.b = *reinterpret_cast<const float4*>(p + 4);
+    return r;
+  }
+  __device__ __forceinline__ static Raw8 zero_raw8() {
+    Raw8 r;
+    r.a = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.b = r.a;
+    return r;
+  }
+  __device__ __forceinline__ static void store_raw8(E* p, Raw8 r) {
+    *reinterpret_cast<float4*>(p) = r.a;
+    *reinterpret_cast<float4*>(p + 4) = r.b;
+  }
+  __device__ __forceinline__ static float to_f32(E x) { return x; }
 };
 
-template <class T> struct ModeOf;
-template <> struct ModeOf<uint16_t> { using type = ModeBF16; static constexpr int DVS = 32; };
-template <> struct ModeOf<float> { using type = ModeF32; static constexpr int DVS = 16; };
+template <class T, int NW> struct __attribute__((aligned(16))) Smem {
+  using E = typename Prec<T>::E;
+  static constexpr int LDK = DK + Prec<T>::PAD;   // rows of 128 features
+  static constexpr int LDT = BT + Prec<T>::PAD;   // rows of 64 tokens
+  E K[BT * LDK];        // K (token, feature)
+  E Q[BT * LDK];        // Q (token, feature)
+  E AT[BT * LDT];       // off-diagonal 16x16 blocks: -A; diagonal blocks: T_bb = (I + A_bb)^-1
+  E P[BT * LDT];        // masked, decayed Q K^T
+  float Ad[4][16][20];  // diagonal 16x16 blocks of A, row-major (rows 16-byte aligned)
+  float W[NW][4][BT];   // per-wave copies of log2-scaled G, gamma, beta, d
+};
 
-template <class T>
-__global__ __launch_bounds__(NT) void prefill_kernel(
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Value of lane `src` (0..3, a constant) of each DPP quad, in all four lanes.
+__device__ __forceinline__ float quad_bcast(float v, int src) {
+  switch (src) {
+    case 0: return dpp_mov<0x00>(v);
+    case 1: return dpp_mov<0x55>(v);
+    case 2: return dpp_mov<0xAA>(v);
+    default: return dpp_mov<0xFF>(v);
+  }
+}
+
+// v moved by a DPP control; lanes without a source (or outside row_mask)
+// read 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the rows' totals are carried forward with row_bcast:15
+// and row_bcast:31.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_or_zero<0x111, 0xf>(v);
+  v += dpp_or_zero<0x112, 0xf>(v);
+  v += dpp_or_zero<0x114, 0xf>(v);
+  v += dpp_or_zero<0x118, 0xf>(v);
+  v += dpp_or_zero<0x142, 0xa>(v);
+  v += dpp_or_zero<0x143, 0xc>(v);
+  return v;
+}
+
+// The 10 lower 16x16 tile pairs (bi, bj): the four diagonal ones first.
+__device__ __forceinline__ void tile_pair(int p, int& bi, int& bj) {
+  constexpr int kI[10] = {0, 1, 2, 3, 1, 2, 3, 2, 3, 3};
+  constexpr int kJ[10] = {0, 1, 2, 3, 0, 1, 2, 0, 1, 0};
+  bi = kI[p];
+  bj = kJ[p];
+}
+
+// NW waves per workgroup, each owning VB blocks of 16 state rows.
+template <class T, int NW, int VB>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int Hk, int Hv, float* state, const uint8_t* __restrict__ has_init, T* __restrict__ o) {
-  using M = typename ModeOf<T>::type;
-  constexpr int DVS = ModeOf<T>::DVS;
-  using SM = Smem<M, DVS>;
-  using E = typename M::elem;
+  using PR = Prec<T>;
+  using E = typename PR::E;
+  using SM = Smem<T, NW>;
+  constexpr int NT = NW * 64;
+  constexpr int DVS = 16 * NW * VB;
+  constexpr int NSL = DK / DVS;
   constexpr int LDK = SM::LDK, LDT = SM::LDT;
-  constexpr int NSL = DK / DVS;            // slices per head
-  constexpr int NVB = DVS / 16;            // 16-row blocks per slice
-  constexpr int NZ = (BT / 16) * NVB;      // (token block, row block) tiles of Z / O
-  constexpr int NSTILE = NVB * (DK / 16);  // tiles of the state slice
-  constexpr int ZPW = (NZ + NW - 1) / NW;
-  constexpr int SPW = NSTILE / NW;
-  static_assert(NSTILE % NW == 0, "state tiles must split evenly over waves");
+  constexpr int KQ_ITEMS = BT * (DK / 8) / NT;   // 16-byte pieces of K and of Q per thread
+  static_assert(NW == 4, "tile-pair assignment assumes 4 waves");
 
   __shared__ SM sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
 
-  int bid = blockIdx.x;
-  const int slice = bid % NSL;
-  bid /= NSL;
-  const int h = bid % Hv;
-  const int s = bid / Hv;
+  // Blocks are dealt to the 8 XCDs round robin; consecutive units (the
+  // slices of one head, then the heads sharing a k-head) go to one XCD so
+  // their shared K and Q reads meet in that XCD's L2.
+  int u = blockIdx.x;
+  if ((gridDim.x & 7) == 0) u = (u & 7) * (gridDim.x >> 3) + (u >> 3);
+  const int slice = u % NSL;
+  u /= NSL;
+  const int h = u % Hv;
+  const int s = u / Hv;
   const int kh = h / (Hv / Hk);
-  const int v0 = slice * DVS;
   const int bos = cu[s], eos = cu[s + 1];
+  int v0[VB];                               // this wave's state rows: v0[b] .. v0[b] + 15
+#pragma unroll
+  for (int b = 0; b < VB; ++b) v0[b] = slice * DVS + 16 * (wave * VB + b);
 
-  constexpr int NS = SM::NS;
-  E* const Thi = sm.T;
-  E* const Tlo = M::kSplit ? sm.T + BT * LDT : nullptr;
-  E* const Phi = sm.P;
-  E* const Plo = M::kSplit ? sm.P + BT * LDT : nullptr;
-  E* const RThi = sm.RT;
-  E* const RTlo = M::kSplit ? sm.RT + DVS * LDT : nullptr;
-  E* const UThi = sm.UT;
-  E* const UTlo = M::kSplit ? sm.UT + DVS * LDT : nullptr;
-  E* const UdThi = sm.UdT;
-  E* const UdTlo = M::kSplit ? sm.UdT + DVS * LDT : nullptr;
-  E* const Shi = sm.S;
-  E* const Slo = M::kSplit ? sm.S + DVS * LDK : nullptr;
-  (void)NS;
-
-  // T and P are lower triangular; their upper 16x16 blocks are read as zeros
-  // by the rounded-up contraction ranges and are never written afterwards.
-  for (int idx = tid; idx < BT * LDT; idx += NT) {
-    Thi[idx] = E(0); Phi[idx] = E(0);
-    if constexpr (M::kSplit) { Tlo[idx] = E(0); Plo[idx] = E(0); }
-  }
-
-  // ---- initial state slice into accumulators (and LDS as an operand)
-  f32x4 Sacc[SPW];
+  // ---- S^T tiles: st[b][cb][e] = S[v0[b] + r16][16 cb + 4 kg + e]
+  f32x4 st[VB][8];
+  float* const sbase = state + ((int64_t)s * Hv + h) * (DK * DK);
   const bool init = has_init == nullptr || has_init[s] != 0;
-  float* const sbase = state + ((int64_t)s * Hv + h) * (DK * DK) + (int64_t)v0 * DK;
 #pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int ts = wave + NW * j;
-    const int tv = ts / (DK / 16), tc = ts % (DK / 16);
+  for (int b = 0; b < VB; ++b)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int vr = 16 * tv + 4 * kg + e, c = 16 * tc + r16;
-      Sacc[j][e] = init ? sbase[vr * DK + c] : 0.f;
+    for (int cb = 0; cb < 8; ++cb) {
+      if (init) {
+        const float4 t = *reinterpret_cast<const float4*>(sbase + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg);
+        st[b][cb] = f32x4{t.x, t.y, t.z, t.w};
+      } else {
+        st[b][cb] = zero4();
+      }
     }
-  }
-#pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int ts = wave + NW * j;
-    const int tv = ts / (DK / 16), tc = ts % (DK / 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) put<M>(Shi, Slo, (16 * tv + 4 * kg + e) * LDK + 16 * tc + r16, Sacc[j][e]);
-  }
 
-  const Opnd<M> opK{sm.K, nullptr, LDK, 1};
-  const Opnd<M> opQ{sm.Q, nullptr, LDK, 1};
-  const Opnd<M> opS{Shi, Slo, LDK, 1};
-  const Opnd<M> opT{Thi, Tlo, LDT, 1};
-  const Opnd<M> opP{Phi, Plo, LDT, 1};
-  const Opnd<M> opRT{RThi, RTlo, LDT, 1};
-  const Opnd<M> opUT{UThi, UTlo, LDT, 1};
-  const Opnd<M> opUdT{UdThi, UdTlo, LDT, 1};
-  // B operand of the state update: element (feature c, token m) = K[m][c]
-  const Opnd<M> opKT = M::kSplit ? Opnd<M>{sm.KT, nullptr, LDT, 1} : Opnd<M>{sm.K, nullptr, 1, LDK};
+  // ---- prefetch registers for one chunk.  Every load is unconditional
+  // (rows past the chunk end read the chunk's last row) and kept in storage
+  // form; rows >= n are zeroed where the data is used, so no load waits on
+  // a branch.
+  typename PR::Raw8 pk[KQ_ITEMS], pq[KQ_ITEMS];
+  E vpre[VB][4][4];
+  float gpre, bpre;
+  auto prefetch = [&](int c0) {
+    const int last = min(BT, eos - c0) - 1;
+#pragma unroll
+    for (int it = 0; it < KQ_ITEMS; ++it) {
+      const int idx = tid + NT * it;
+      const int row = min(idx >> 4, last), c8 = (idx & 15) * 8;
+      const int64_t off = ((int64_t)(c0 + row) * Hk + kh) * DK + c8;
+      pk[it] = PR::load_raw8(k + off);
+      pq[it] = PR::load_raw8(q + off);
+    }
+#pragma unroll
+    for (int b = 0; b < VB; ++b)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = min(16 * ib + 4 * kg + e, last);
+          vpre[b][ib][e] = v[((int64_t)(c0 + row) * Hv + h) * DK + v0[b] + r16];
+        }
+    const int row = min(lane, last);
+    gpre = g[(int64_t)(c0 + row) * Hv + h];
+    bpre = beta[(int64_t)(c0 + row) * Hv + h];
+  };
+
+  if (bos < eos) prefetch(bos);
+
+  float* const WL = sm.W[wave][0];    // log2-scaled G
+  float* const Wgam = sm.W[wave][1];
+  float* const Wb = sm.W[wave][2];
+  float* const Wd = sm.W[wave][3];
 
   for (int c0 = bos; c0 < eos; c0 += BT) {
     const int n = min(BT, eos - c0);
-    __syncthreads();  // the previous chunk is done with every LDS buffer
+    __syncthreads();  // the previous chunk is done with K, Q, AT, P, Ad
 
-    // ---- 1. stage K, K^T, Q, V slice, g, beta
-    for (int it = tid; it < BT * (DK / 8); it += NT) {
-      const int row = it / (DK / 8), c8 = (it % (DK / 8)) * 8;
-      float kv[8], qv[8];
-      if (row < n) {
-        const int64_t off = ((int64_t)(c0 + row) * Hk + kh) * DK + c8;
-        Act<T>::load8(k + off, kv);
-        Act<T>::load8(q + off, qv);
-      } else {
+    // ---- 1. stage K and Q; keep this chunk's V, g, beta; prefetch the next
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { kv[i] = 0.f; qv[i] = 0.f; }
+    for (int it = 0; it < KQ_ITEMS; ++it) {
+      const int idx = tid + NT * it;
+      const int row = idx >> 4, c8 = (idx & 15) * 8;
+      const bool ok = row < n;
+      PR::store_raw8(&sm.K[row * LDK + c8], ok ? pk[it] : PR::zero_raw8());
+      PR::store_raw8(&sm.Q[row * LDK + c8], ok ? pq[it] : PR::zero_raw8());
+    }
+    float vv[VB][4][4];
+#pragma unroll
+    for (int b = 0; b < VB; ++b)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vv[b][ib][e] = (16 * ib + 4 * kg + e < n) ? PR::to_f32(vpre[b][ib][e]) : 0.f;
+    const float gl = lane < n ? gpre : 0.f, bl = lane < n ? bpre : 0.f;
+    if (c0 + BT < eos) prefetch(c0 + BT);
+
+    // cumulative log decay over the chunk, in every wave (lane = token)
+    const float L = wave_prefix_sum(gl) * kLog2e;
+    const float Llast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), n - 1));
+    WL[lane] = L;
+    Wgam[lane] = exp2f(L);
+    Wb[lane] = bl;
+    Wd[lane] = lane < n ? exp2f(Llast - L) : 0.f;
+    const float gamma_last = exp2f(Llast);
+    __syncthreads();
+
+    // ---- 2a. Z = K S0^T and QS = Q S0^T for this wave's rows.  The K and Q
+    //          fragments of contraction step t+1 are read while step t runs.
+    f32x4 z[VB][4], qs[VB][4];
+#pragma unroll
+    for (int b = 0; b < VB; ++b)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) { z[b][ib] = zero4(); qs[b][ib] = zero4(); }
+    {
+      typename PR::F32 fk[2][4], fq[2][4];
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        fk[0][ib] = PR::lds32(sm.K, LDK, 16 * ib + r16, 0, kg);
+        fq[0][ib] = PR::lds32(sm.Q, LDK, 16 * ib + r16, 0, kg);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (M::kSplit) {
-          const uint16_t kb = static_cast<uint16_t>(f32_to_bf16(kv[i]));  // exact: kv came from bf16
-          sm.K[row * LDK + c8 + i] = kb;
-          sm.KT[(c8 + i) * LDT + row] = kb;
-          sm.Q[row * LDK + c8 + i] = static_cast<uint16_t>(f32_to_bf16(qv[i]));
-        } else {
-          sm.K[row * LDK + c8 + i] = kv[i];
-          sm.Q[row * LDK + c8 + i] = qv[i];
+      for (int t = 0; t < 4; ++t) {
+        const int cur = t & 1, nxt = cur ^ 1;
+        if (t < 3) {
+#pragma unroll
+          for (int ib = 0; ib < 4; ++ib) {
+            fk[nxt][ib] = PR::lds32(sm.K, LDK, 16 * ib + r16, 32 * (t + 1), kg);
+            fq[nxt][ib] = PR::lds32(sm.Q, LDK, 16 * ib + r16, 32 * (t + 1), kg);
+          }
         }
-      }
-    }
-    for (int it = tid; it < BT * (DVS / 8); it += NT) {
-      const int row = it / (DVS / 8), c8 = (it % (DVS / 8)) * 8;
-      float vv[8];
-      if (row < n) {
-        Act<T>::load8(v + ((int64_t)(c0 + row) * Hv + h) * DK + v0 + c8, vv);
-      } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vv[i] = 0.f;
-      }
+        for (int b = 0; b < VB; ++b) {
+          const auto bs = PR::reg32(st[b][2 * t], st[b][2 * t + 1]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (M::kSplit) sm.V[row * DVS + c8 + i] = static_cast<uint16_t>(f32_to_bf16(vv[i]));
-        else sm.V[row * DVS + c8 + i] = vv[i];
-      }
-    }
-    if (tid < BT) {
-      const bool ok = tid < n;
-      sm.G[tid] = ok ? g[(int64_t)(c0 + tid) * Hv + h] : 0.f;
-      sm.Beta[tid] = ok ? beta[(int64_t)(c0 + tid) * Hv + h] : 0.f;
-    }
-    __syncthreads();
-
-    // ---- 2. cumulative log-decay (wave 0) and K K^T, Q K^T lower tiles
-    if (wave == 0) {
-      float gv = sm.G[lane];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float t = __shfl_up(gv, off, 64);
-        if (lane >= off) gv += t;
-      }
-      const float glast = __shfl(gv, n - 1, 64);
-      sm.G[lane] = gv;
-      sm.Gam[lane] = expf(gv);
-      sm.D[lane] = lane < n ? expf(glast - gv) : 0.f;
-      if (lane == 0) sm.gamma_last = expf(glast);
-    }
-    // 10 lower tiles of K K^T (jobs 0..9) and of Q K^T (jobs 10..19)
-    constexpr int NJOB = 20;
-    constexpr int JPW = (NJOB + NW - 1) / NW;
-    f32x4 jacc[JPW];
-#pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int job = wave + NW * jj;
-      jacc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (job < NJOB) {
-        const int t = job % 10;
-        int bi = 0;
-        while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
-        const int bj = t - bi * (bi + 1) / 2;
-        jacc[jj] = mma<M>(jacc[jj], job < 10 ? opK : opQ, 16 * bi, opK, 16 * bj, 0, DK, lane);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int jj = 0; jj < JPW; ++jj) {
-      const int job = wave + NW * jj;
-      if (job < NJOB) {
-        const int t = job % 10;
-        int bi = 0;
-        while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
-        const int bj = t - bi * (bi + 1) / 2;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * bi + 4 * kg + e, j = 16 * bj + r16;
-          const float decay = j <= i ? expf(sm.G[i] - sm.G[j]) : 0.f;
-          if (job < 10) {
-            sm.A[i * (BT + 1) + j] = j < i ? sm.Beta[i] * decay * jacc[jj][e] : 0.f;
-          } else {
-            put<M>(Phi, Plo, i * LDT + j, decay * jacc[jj][e]);
+          for (int ib = 0; ib < 4; ++ib) {
+            z[b][ib] = PR::mma32(fk[cur][ib], bs, z[b][ib]);
+            qs[b][ib] = PR::mma32(fq[cur][ib], bs, qs[b][ib]);
           }
         }
       }
     }
-    __syncthreads();
 
-    // ---- 3. T = (I + A)^-1
-    // 3a. diagonal 16x16 blocks, one per 16-lane group of wave 0: lane
-    //     (blk, col) forward-substitutes column col of block blk.
-    if (wave == 0) {
-      const int blk = kg, col = r16, base = 16 * blk;
-      float xcol[16];
+    // ---- 2b. tile pairs of K K^T and Q K^T -> -A, A_bb, P.  Wave w takes
+    //          diagonal pair w (and inverts it) plus off-diagonal pairs
+    //          4 + w and, for w < 2, 8 + w.
+    for (int p = wave; p < 10; p = (p < 4) ? p + 4 : (p < 6 ? p + 4 : 10)) {
+      int bi, bj;
+      tile_pair(p, bi, bj);
+      f32x4 kk = zero4(), qk = zero4();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == col) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < i; ++j) acc -= sm.A[(base + i) * (BT + 1) + base + j] * xcol[j];
-        xcol[i] = acc;
+      for (int kb = 0; kb < DK; kb += 32) {
+        const auto bk = PR::lds32(sm.K, LDK, 16 * bj + r16, kb, kg);
+        kk = PR::mma32(PR::lds32(sm.K, LDK, 16 * bi + r16, kb, kg), bk, kk);
+        qk = PR::mma32(PR::lds32(sm.Q, LDK, 16 * bi + r16, kb, kg), bk, qk);
       }
+      // rows i = 16 bi + 4 kg + e (4 consecutive tokens), column j = 16 bj + r16
+      const float4 Li = *reinterpret_cast<const float4*>(&WL[16 * bi + 4 * kg]);
+      const float4 Bi = *reinterpret_cast<const float4*>(&Wb[16 * bi + 4 * kg]);
+      const float Lj = WL[16 * bj + r16];
+      const float li[4] = {Li.x, Li.y, Li.z, Li.w};
+      const float bb4[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) put<M>(Thi, Tlo, (base + i) * LDT + base + col, xcol[i]);
-    }
-    __syncthreads();
-    // 3b. off-diagonal blocks by block forward substitution, level by level:
-    //     T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj   (block indices, i - j = lvl)
-    for (int lvl = 1; lvl < 4; ++lvl) {
-      const int bi = lvl + wave, bj = wave;
-      const bool active = bi < 4;
-      float* X = sm.X + wave * (16 * 17);
-      if (active) {
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * bi + 4 * kg + e, j = 16 * bj + r16;
+        const float dec = j <= i ? exp2f(li[e] - Lj) : 0.f;
+        PR::put(&sm.P[i * LDT + j], dec * qk[e]);
+        const float a = j < i ? bb4[e] * dec * kk[e] : 0.f;
+        if (bi == bj) sm.Ad[bi][i - 16 * bi][j - 16 * bj] = a;
+        else PR::put(&sm.AT[i * LDT + j], -a);
+      }
+      if (bi == bj) {
+        // T_bb = (I + A_bb)^-1 by forward substitution.  Lane (c, q) =
+        // (lane / 4, lane % 4) owns rows q, q+4, q+8, q+12 of column c; the
+        // four lanes of a column form a DPP quad, and x_j, once final, is
+        // broadcast within the quad from the lane that owns row j.  Terms
+        // with j >= i vanish because A_bb is strictly lower triangular.
+        __builtin_amdgcn_wave_barrier();   // A_bb above was written by this wave
+        const int c = lane >> 2, qd = lane & 3;
+        float arow[4][16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = 4 * kg + e, cc = r16;
-          float acc = 0.f;
-          for (int bm = bj; bm < bi; ++bm) {
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int m = 0; m < 16; ++m)
-              acc += sm.A[(16 * bi + rr) * (BT + 1) + 16 * bm + m] *
-                     get<M>(Thi, Tlo, (16 * bm + m) * LDT + 16 * bj + cc);
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const float4 t = *reinterpret_cast<const float4*>(&sm.Ad[bi][qd + 4 * m][4 * j4]);
+            arow[m][4 * j4] = t.x; arow[m][4 * j4 + 1] = t.y;
+            arow[m][4 * j4 + 2] = t.z; arow[m][4 * j4 + 3] = t.w;
           }
-          X[rr * 17 + cc] = acc;
+        float x[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = (qd + 4 * m == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float xj = quad_bcast(x[j >> 2], j & 3);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) x[m] = __builtin_fmaf(-arow[m][j], xj, x[m]);
         }
-      }
-      __syncthreads();
-      if (active) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = 4 * kg + e, cc = r16;
-          float acc = 0.f;
-#pragma unroll
-          for (int m = 0; m < 16; ++m)
-            acc += get<M>(Thi, Tlo, (16 * bi + rr) * LDT + 16 * bi + m) * X[m * 17 + cc];
-          put<M>(Thi, Tlo, (16 * bi + rr) * LDT + 16 * bj + cc, -acc);
-        }
-      }
-      __syncthreads();
-    }
-
-    // ---- 4. Z = K S0^T and QS = Q S0^T; R = diag(b) (V - diag(gamma) Z)
-    f32x4 QS[ZPW];
-#pragma unroll
-    for (int jj = 0; jj < ZPW; ++jj) {
-      const int tz = wave + NW * jj;
-      QS[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (tz < NZ) {
-        const int ti = tz / NVB, tv = tz % NVB;
-        f32x4 z = mma<M>(f32x4{0.f, 0.f, 0.f, 0.f}, opK, 16 * ti, opS, 16 * tv, 0, DK, lane);
-        QS[jj] = mma<M>(QS[jj], opQ, 16 * ti, opS, 16 * tv, 0, DK, lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * ti + 4 * kg + e, vr = 16 * tv + r16;
-          float vv;
-          if constexpr (M::kSplit) vv = bf16_to_f32(sm.V[i * DVS + vr]);
-          else vv = sm.V[i * DVS + vr];
-          const float rv = sm.Beta[i] * (vv - sm.Gam[i] * z[e]);
-          put<M>(RThi, RTlo, vr * LDT + i, rv);
-        }
+        for (int m = 0; m < 4; ++m) PR::put(&sm.AT[(16 * bi + qd + 4 * m) * LDT + 16 * bi + c], x[m]);
       }
     }
     __syncthreads();
 
-    // ---- 5. U = T R  (T is lower triangular: row block ti needs tokens < 16 (ti+1))
+    // ---- 3. R, then (I + A) U = R by block forward substitution:
+    //         U_i = T_ii (R_i + sum_{m<i} (-A_im) U_m)
+    float gam4[4][4], b4[4][4], d4[4][4];
 #pragma unroll
-    for (int jj = 0; jj < ZPW; ++jj) {
-      const int tz = wave + NW * jj;
-      if (tz < NZ) {
-        const int ti = tz / NVB, tv = tz % NVB;
-        const int kend = ((16 * (ti + 1) + M::KS - 1) / M::KS) * M::KS;
-        f32x4 u = mma<M>(f32x4{0.f, 0.f, 0.f, 0.f}, opT, 16 * ti, opRT, 16 * tv, 0, kend, lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * ti + 4 * kg + e, vr = 16 * tv + r16;
-          put<M>(UThi, UTlo, vr * LDT + i, u[e]);
-          put<M>(UdThi, UdTlo, vr * LDT + i, u[e] * sm.D[i]);
-        }
-      }
+    for (int ib = 0; ib < 4; ++ib) {
+      const float4 ga = *reinterpret_cast<const float4*>(&Wgam[16 * ib + 4 * kg]);
+      const float4 bt = *reinterpret_cast<const float4*>(&Wb[16 * ib + 4 * kg]);
+      const float4 dd = *reinterpret_cast<const float4*>(&Wd[16 * ib + 4 * kg]);
+      gam4[ib][0] = ga.x; gam4[ib][1] = ga.y; gam4[ib][2] = ga.z; gam4[ib][3] = ga.w;
+      b4[ib][0] = bt.x; b4[ib][1] = bt.y; b4[ib][2] = bt.z; b4[ib][3] = bt.w;
+      d4[ib][0] = dd.x; d4[ib][1] = dd.y; d4[ib][2] = dd.z; d4[ib][3] = dd.w;
     }
-    __syncthreads();
-
-    // ---- 6. O = diag(gamma) QS + P U, and S = gamma_last S0 + (U^T diag(d)) K
+    f32x4 uu[VB][4];
 #pragma unroll
-    for (int jj = 0; jj < ZPW; ++jj) {
-      const int tz = wave + NW * jj;
-      if (tz < NZ) {
-        const int ti = tz / NVB, tv = tz % NVB;
-        const int kend = ((16 * (ti + 1) + M::KS - 1) / M::KS) * M::KS;
-        f32x4 pu = mma<M>(f32x4{0.f, 0.f, 0.f, 0.f}, opP, 16 * ti, opUT, 16 * tv, 0, kend, lane);
+    for (int ib = 0; ib < 4; ++ib) {
+      f32x4 rr[VB];
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[b][e] = b4[ib][e] * (vv[b][ib][e] - gam4[ib][e] * z[b][ib][e]);
+      if (ib >= 2) {   // blocks 0 and 1 together as one 32-wide step
+        const auto a01 = PR::lds32(sm.AT, LDT, 16 * ib + r16, 0, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) rr[b] = PR::mma32(a01, PR::reg32(uu[b][0], uu[b][1]), rr[b]);
+      }
+      if (ib == 1 || ib == 3) {
+        const auto am = PR::lds16(sm.AT, LDT, 16 * ib + r16, 16 * (ib - 1), kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) rr[b] = PR::mma16(am, PR::reg16(uu[b][ib - 1]), rr[b]);
+      }
+      const auto td = PR::lds16(sm.AT, LDT, 16 * ib + r16, 16 * ib, kg);
+#pragma unroll
+      for (int b = 0; b < VB; ++b) uu[b][ib] = PR::mma16(td, PR::reg16(rr[b]), zero4());
+    }
+
+    // ---- 4. O = diag(gamma) QS + P U
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      f32x4 pu[VB];
+#pragma unroll
+      for (int b = 0; b < VB; ++b) pu[b] = zero4();
+      if (ib >= 1) {
+        const auto p01 = PR::lds32(sm.P, LDT, 16 * ib + r16, 0, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) pu[b] = PR::mma32(p01, PR::reg32(uu[b][0], uu[b][1]), pu[b]);
+      }
+      if (ib == 3) {
+        const auto p23 = PR::lds32(sm.P, LDT, 16 * ib + r16, 32, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) pu[b] = PR::mma32(p23, PR::reg32(uu[b][2], uu[b][3]), pu[b]);
+      } else if (ib != 1) {   // ib == 0: block 0; ib == 2: block 2
+        const auto pd = PR::lds16(sm.P, LDT, 16 * ib + r16, 16 * ib, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) pu[b] = PR::mma16(pd, PR::reg16(uu[b][ib]), pu[b]);
+      }
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 16 * ti + 4 * kg + e, vr = 16 * tv + r16;
+          const int i = 16 * ib + 4 * kg + e;
           if (i < n) {
-            const float ov = sm.Gam[i] * QS[jj][e] + pu[e];
-            Act<T>::store1(o + ((int64_t)(c0 + i) * Hv + h) * DK + v0 + vr, ov);
+            const float ov = gam4[ib][e] * qs[b][ib][e] + pu[b][e];
+            Act<T>::store1(o + ((int64_t)(c0 + i) * Hv + h) * DK + v0[b] + r16, ov);
           }
         }
-      }
     }
-    const float gl = sm.gamma_last;
+
+    // ---- 5. S^T <- gamma_last S^T + K^T diag(d) U
+    typename PR::F32 du01[VB], du23[VB];
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int ts = wave + NW * j;
-      const int tv = ts / (DK / 16), tc = ts % (DK / 16);
-      f32x4 acc;
+    for (int b = 0; b < VB; ++b) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = gl * Sacc[j][e];
-      Sacc[j] = mma<M>(acc, opUdT, 16 * tv, opKT, 16 * tc, 0, BT, lane);
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) put<M>(Shi, Slo, (16 * tv + 4 * kg + e) * LDK + 16 * tc + r16, Sacc[j][e]);
+        for (int e = 0; e < 4; ++e) uu[b][mb][e] *= d4[mb][e];
+      du01[b] = PR::reg32(uu[b][0], uu[b][1]);
+      du23[b] = PR::reg32(uu[b][2], uu[b][3]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const auto kt0 = PR::ldsT32(sm.K, LDK, 16 * cb, 0, lane);
+      const auto kt1 = PR::ldsT32(sm.K, LDK, 16 * cb, 32, lane);
+#pragma unroll
+      for (int b = 0; b < VB; ++b) {
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = gamma_last * st[b][cb][e];
+        acc = PR::mma32(kt0, du01[b], acc);
+        st[b][cb] = PR::mma32(kt1, du23[b], acc);
+      }
     }
   }
 
-  // ---- final state slice
+  // ---- final state
 #pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int ts = wave + NW * j;
-    const int tv = ts / (DK / 16), tc = ts % (DK / 16);
+  for (int b = 0; b < VB; ++b)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sbase[(16 * tv + 4 * kg + e) * DK + 16 * tc + r16] = Sacc[j][e];
-  }
+    for (int cb = 0; cb < 8; ++cb)
+      *reinterpret_cast<float4*>(sbase + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg) =
+          make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
+}
+
+template <class T, int NW, int VB>
+hipError_t launch_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                    const int32_t* cu, int nseq, int Hk, int Hv, float* state,
+                    const uint8_t* has_init, void* o, hipStream_t st) {
+  const dim3 grid(nseq * Hv * (DK / (16 * NW * VB)));
+  hipLaunchKernelGGL((prefill_kernel<T, NW, VB>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(q),
+                     static_cast<const T*>(k), static_cast<const T*>(v), g, beta, cu, Hk, Hv, state,
+                     has_init, static_cast<T*>(o));
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -479,19 +578,13 @@ __global__ __launch_bounds__(NT) void prefill_kernel(
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int act, const float* g,
                           const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
                           float* state, const uint8_t* has_init, void* o, hipStream_t st) {
-  if (act == GDN_F32) {
-    dim3 grid(nseq * Hv * (DK / ModeOf<float>::DVS));
-    hipLaunchKernelGGL(prefill_kernel<float>, grid, dim3(NT), 0, st, static_cast<const float*>(q),
-                       static_cast<const float*>(k), static_cast<const float*>(v), g, beta, cu, Hk,
-                       Hv, state, has_init, static_cast<float*>(o));
-  } else {
-    dim3 grid(nseq * Hv * (DK / ModeOf<uint16_t>::DVS));
-    hipLaunchKernelGGL(prefill_kernel<uint16_t>, grid, dim3(NT), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), g, beta, cu, Hk, Hv, state, has_init,
-                       static_cast<uint16_t*>(o));
-  }
-  return hipGetLastError();
+  if (act == GDN_F32) return launch_t<float, 4, 1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
+  // Two 16-row blocks per wave (one workgroup per head) share every K / Q
+  // fragment between two MFMAs; with fewer than ~200 (sequence, head) units
+  // the chip is better filled by one block per wave (two workgroups per head).
+  if ((long long)nseq * Hv >= 192)
+    return launch_t<uint16_t, 4, 2>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
+  return launch_t<uint16_t, 4, 1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
 }
 
 }  // namespace gdn

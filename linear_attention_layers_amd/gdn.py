@@ -22,6 +22,22 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
+
+def _hip_runtimes():
+    """Distinct HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+# The library must share torch's HIP runtime: if it was loaded before torch,
+# a second runtime is mapped and device pointers and streams would not match.
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are loaded (" + ", ".join(_hip_runtimes()) + "); "
+                      "import torch before loading libgdn.so")
+
 GDN_F32 = 0
 GDN_BF16 = 1
 CHUNK_LEN = 64

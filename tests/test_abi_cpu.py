@@ -8,6 +8,7 @@ import re
 
 import numpy as np
 import pytest
+import torch  # noqa: F401  (loaded before libgdn.so so both use torch's HIP runtime)
 
 from oracle import gdn_oracle as O
 
