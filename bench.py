@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -117,9 +120,22 @@ def main():
         sys.exit(2)
 
     import torch
-    from linear_attention_layers_amd import gdn, inputs
 
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
+        return
+
+    from linear_attention_layers_amd import gdn, inputs
+
     lb = inputs.varlen_prefill()
     Hk, Hv, C, N = lb.geo.Hk, lb.geo.Hv, lb.geo.C, lb.N
     x = lb.x.to(dev)
