@@ -15,8 +15,8 @@
 // WY factor; here it is reached by solving (I + A) U = R blockwise.)
 //
 // Work split.  Rows of S (the dv index) evolve independently.  A workgroup
-// owns one (sequence, v-head, slice of 16*NW state rows) and walks the
-// sequence's chunks in order; wave w owns 16 state rows and holds them
+// owns one (sequence, v-head, slice of state rows) and walks the sequence's
+// chunks in order; a wave owns 16-row blocks of the state and holds them
 // TRANSPOSED (S^T, 8 tiles of 16x16) in MFMA accumulators.  An accumulator
 // tile holds element [4*(lane/16) + e][lane % 16], which is exactly the
 // B-operand layout of the next product (contraction index = tile row), so
@@ -25,13 +25,14 @@
 // K^T operand of the state update is read from K with the transposing LDS
 // load ds_read_b64_tr_b16.
 //
-// Per chunk (3 barriers): stage K, Q; then every wave computes Z = K S0^T and
-// Q S0^T for its rows plus its share of the 10 lower 16x16 tile pairs of
-// K K^T and Q K^T (scaled into -A, the diagonal blocks of A, and P), and the
-// waves holding a diagonal pair invert that unit-lower-triangular block in
-// float32; then U_i = T_ii (R_i - sum_{m<i} A_im U_m) block by block, O and
-// the state update.  The next chunk's K, Q, V, g and beta are loaded into
-// registers while the current chunk computes.
+// Two schedules.  prefill_kernel (float32 activations): every wave stages,
+// builds its share of the 10 lower 16x16 tile pairs of K K^T and Q K^T
+// (scaled into -A, the diagonal blocks of A, and P) and of the diagonal
+// inverses, then runs the state chain; three barriers per chunk, the next
+// chunk's inputs prefetched into registers.  prefill_ws_kernel (bf16
+// activations): producer waves build the state-independent factors one
+// chunk ahead while consumer waves run the state chain (described at that
+// kernel).
 //
 // Precision.  bf16 activations: every contraction is one bf16 MFMA pass
 // (v_mfma_f32_16x16x32_bf16, or 16x16x16 for the 16-wide block solve) with
@@ -562,6 +563,598 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(
           make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
 }
 
+// ---------------------------------------------------------------------------
+// Warp-specialised variant (bf16 activations).  The part of a chunk that
+// does not depend on the state (staging K and Q, the tile pairs of K K^T and
+// Q K^T, the decays, -A, P and the diagonal inverses) is built ahead of the
+// state chain by four producer waves, while four consumer waves own the
+// state and run the chain (Z, R, U, the state update, O) of the current
+// chunk.  Each SIMD hosts one wave of each role, so the LDS and MFMA
+// latencies of one role are covered by the other's work.  In iteration c
+// the consumers run chunk c while the producers build the factors of chunk
+// c+1 and stage K, Q and the gate vectors of chunk c+2: K, Q and the gate
+// vectors are triple-buffered in LDS, the factors double-buffered, and one
+// barrier ends each iteration.
+//
+// Global accesses go through raw buffer resources that span exactly the
+// valid tokens of the chunk, so the hardware range check zero-fills loads
+// of tail rows and drops stores to them; no lane masks or address clamps.
+// O is formed transposed (the operands of Q S^T and P U swapped), which
+// gives each lane four consecutive dv values of one token: 8-byte stores.
+// The pair products are formed transposed for the same reason: each lane
+// writes four consecutive columns of P and -A.
+
+constexpr int kBufDword3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr int kOrderMax = 64;            // batches up to this size run longest first
+
+// The size is made wave-uniform explicitly so the descriptor lives in
+// scalar registers (a vector-register descriptor costs a waterfall loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, __builtin_amdgcn_readfirstlane(bytes),
+                                           kBufDword3);
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// K and Q tiles (64 tokens x 128 features, bf16) are stored unpadded with
+// the 8-byte granules of row r XOR-permuted by sig(r) = 4 (r % 8) +
+// 2 ((r / 8) % 2).  A fragment read (32 lanes: 16 rows x 2 granules) and a
+// transposing read (32 lanes: 8 rows x 4 consecutive granules) then both
+// touch each of the 64 LDS banks exactly once; no plain row padding does
+// that for both patterns.  Returns the element offset of granule g of row r.
+__device__ __forceinline__ int kq_at(int r, int g) {
+  return 4 * (32 * r + (g ^ (4 * (r & 7) + 2 * ((r >> 3) & 1))));
+}
+
+struct __attribute__((aligned(16))) SmemWS {
+  static constexpr int LDT = BT + 8;   // rows of 64 tokens (bf16)
+  uint16_t K[3][BT * DK];
+  uint16_t Q[3][BT * DK];
+  uint16_t AT[2][BT * LDT];   // off-diagonal 16x16 blocks: -A; diagonal blocks: T_bb
+  uint16_t P[2][BT * LDT];
+  float W[3][4][BT];          // per chunk: log2-scaled G, gamma, beta, d
+  float Ad[4][16][20];        // diagonal block of A of each producer wave
+  int len[kOrderMax];         // sequence lengths, for the longest-first order
+  int pick;
+};
+
+// Fragment of a swizzled K / Q tile: rows row.., contraction kb.. (as
+// Prec<uint16_t>::lds32 on a row-major tile).
+__device__ __forceinline__ Prec<uint16_t>::F32 kq_frag(const uint16_t* p, int row, int kb, int kg) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p + kq_at(row, (kb >> 2) + kg));
+  const uint2 b = *reinterpret_cast<const uint2*>(p + kq_at(row, (kb >> 2) + 4 + kg));
+  Prec<uint16_t>::F32 f;
+  f.v = make_uint4(a.x, a.y, b.x, b.y);
+  return f;
+}
+
+// Transposed fragment of a swizzled K tile (as Prec<uint16_t>::ldsT32).
+__device__ __forceinline__ Prec<uint16_t>::F32 kq_fragT(const uint16_t* p, int c0, int kb, int lane) {
+  const int sl = lane & 15, kg = lane >> 4;
+  const int r = kb + 4 * kg + (sl >> 2), g = (c0 >> 2) + (sl & 3);
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + kq_at(r, g)));
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + kq_at(r + 16, g)));
+  const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
+  Prec<uint16_t>::F32 f;
+  f.v = make_uint4(ux.x, ux.y, uy.x, uy.y);
+  return f;
+}
+
+template <int VB>
+__global__ __launch_bounds__(512) void prefill_ws_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    int Hk, int Hv, float* state, const uint8_t* __restrict__ has_init, uint16_t* __restrict__ o) {
+  using PR = Prec<uint16_t>;
+  constexpr int DVS = 64 * VB;   // state rows per workgroup (4 consumer waves)
+  constexpr int NSL = DK / DVS;
+  constexpr int LDT = SmemWS::LDT;
+  constexpr int KQ_ITEMS = BT * (DK / 8) / 256;   // 16-byte pieces per producer thread
+
+  __shared__ SmemWS sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int rw = wave & 3;   // index of the wave within its role
+
+  // Work item -> (sequence, v-head, slice).  Blocks are dispatched in
+  // index order, so the sequences are taken longest first (for batches of
+  // up to kOrderMax sequences): the longest sequence, whose chunks run one
+  // after another, starts in the first wave of workgroups.  Within a
+  // sequence, block b runs on XCD b % 8 (round-robin dispatch); item
+  // i = (b % 8) * (items / 8) + b / 8 keeps the heads sharing a k-head, which
+  // read the same K and Q, on one XCD and its L2.
+  const int items = Hv * NSL;
+  const int nseq = gridDim.x / items;
+  const int rank = blockIdx.x / items;
+  int item = blockIdx.x % items;
+  if ((items & 7) == 0) item = (item & 7) * (items >> 3) + (item >> 3);
+  int s = rank;
+  if (nseq > 1 && nseq <= kOrderMax) {
+    if (tid < nseq) sm.len[tid] = cu[tid + 1] - cu[tid];
+    __syncthreads();
+    if (tid < nseq) {
+      const int mine = sm.len[tid];
+      int r = 0;
+      for (int t = 0; t < nseq; ++t) {
+        const int other = sm.len[t];
+        r += (other > mine || (other == mine && t < tid)) ? 1 : 0;
+      }
+      if (r == rank) sm.pick = tid;
+    }
+    __syncthreads();
+    s = __builtin_amdgcn_readfirstlane(sm.pick);
+  }
+  const int slice = item % NSL;
+  const int h = item / NSL;
+  const int kh = h / (Hv / Hk);
+  const int bos = cu[s], eos = cu[s + 1];
+  const int nc = eos > bos ? (eos - bos + BT - 1) / BT : 0;
+  // valid tokens of chunk c (0 past the end)
+  auto chunk_len = [&](int c) { return max(0, min(BT, eos - (bos + BT * c))); };
+
+  if (wave >= 4) {
+    // ================================================================ producers
+    if (nc == 0) return;
+    const int ptid = tid - 256;
+    u32x4 pk[KQ_ITEMS], pq[KQ_ITEMS];
+    float gr = 0.f, br = 0.f;
+    auto load_kq = [&](int c) {
+      const int64_t c0 = bos + BT * c;
+      const int bytes = chunk_len(c) * Hk * DK * 2;
+      const auto rk = buf_rsrc(k + c0 * Hk * DK, bytes);
+      const auto rq = buf_rsrc(q + c0 * Hk * DK, bytes);
+#pragma unroll
+      for (int it = 0; it < KQ_ITEMS; ++it) {
+        const int idx = ptid + 256 * it;
+        const int off = (((idx >> 4) * Hk + kh) * DK + (idx & 15) * 8) * 2;
+        pk[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+        pq[it] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      }
+    };
+    auto stage_kq = [&](int buf) {
+#pragma unroll
+      for (int it = 0; it < KQ_ITEMS; ++it) {
+        const int idx = ptid + 256 * it;
+        const int e = kq_at(idx >> 4, 2 * (idx & 15));
+        *reinterpret_cast<u32x4*>(&sm.K[buf][e]) = pk[it];
+        *reinterpret_cast<u32x4*>(&sm.Q[buf][e]) = pq[it];
+      }
+    };
+    // gate vectors: one token per lane (wave rw == 0 only)
+    auto load_gates = [&](int c) {
+      const int64_t c0 = bos + BT * c;
+      const int bytes = chunk_len(c) * Hv * 4;
+      const int off = (lane * Hv + h) * 4;
+      gr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(g + c0 * Hv, bytes), off, 0, 0));
+      br = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buf_rsrc(beta + c0 * Hv, bytes), off, 0, 0));
+    };
+    // cumulative log2-decay of chunk c and the vectors derived from it;
+    // lanes past the chunk's end hold g = beta = 0
+    auto scan = [&](int c) {
+      const int n = chunk_len(c);
+      const float L = wave_prefix_sum(gr) * kLog2e;
+      const float Llast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), max(n, 1) - 1));
+      float* Wc = &sm.W[c % 3][0][0];
+      Wc[lane] = L;
+      Wc[BT + lane] = __builtin_amdgcn_exp2f(L);
+      Wc[2 * BT + lane] = br;
+      Wc[3 * BT + lane] = lane < n ? __builtin_amdgcn_exp2f(Llast - L) : 0.f;
+    };
+    // tile pair (bi, bj), bi >= bj, of K/Q buffer kb with gate vectors wb:
+    // lane (r16, kg) forms rows i = 16 bi + r16, columns j = 16 bj + 4 kg + e
+    // of P and A (transposed products: K_bj-rows as the A operand)
+    auto do_pair = [&](int p, int kb, int ab, bool diag) {
+      int bi, bj;
+      tile_pair(p, bi, bj);
+      const uint16_t* Kb = sm.K[kb];
+      const uint16_t* Qb = sm.Q[kb];
+      typename PR::F32 fa[4], fq[4], fb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fb[t] = kq_frag(Kb, 16 * bj + r16, 32 * t, kg);
+        fq[t] = kq_frag(Qb, 16 * bi + r16, 32 * t, kg);
+        fa[t] = diag ? fb[t] : kq_frag(Kb, 16 * bi + r16, 32 * t, kg);
+      }
+      f32x4 kk = zero4(), qk = zero4();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        kk = PR::mma32(fb[t], fa[t], kk);
+        qk = PR::mma32(fb[t], fq[t], qk);
+      }
+      const float* Wl = &sm.W[kb][0][0];
+      const int i = 16 * bi + r16, j0 = 16 * bj + 4 * kg;
+      const float Li = Wl[i], bti = Wl[2 * BT + i];
+      const float4 Lj = *reinterpret_cast<const float4*>(&Wl[j0]);
+      const float lj[4] = {Lj.x, Lj.y, Lj.z, Lj.w};
+      float pv[4], av[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dec = j0 + e <= i ? __builtin_amdgcn_exp2f(Li - lj[e]) : 0.f;
+        pv[e] = dec * qk[e];
+        av[e] = j0 + e < i ? bti * dec * kk[e] : 0.f;
+      }
+      *reinterpret_cast<u32x2*>(&sm.P[ab][i * LDT + j0]) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+      if (diag)
+        *reinterpret_cast<float4*>(&sm.Ad[rw][r16][4 * kg]) = make_float4(av[0], av[1], av[2], av[3]);
+      else
+        *reinterpret_cast<u32x2*>(&sm.AT[ab][i * LDT + j0]) =
+            u32x2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
+    };
+    // T_bb = (I + A_bb)^-1 of this wave's diagonal block b = rw, by forward
+    // substitution.  Lane (c, q) = (lane / 4, lane % 4) owns rows q, q+4,
+    // q+8, q+12 of column c; the four lanes of a column form a DPP quad and
+    // x_j, once final, is broadcast from the lane owning row j.  Terms with
+    // j >= i vanish: A_bb is strictly lower triangular.
+    auto invert_diag = [&](int ab) {
+      const int c = lane >> 2, qd = lane & 3, bb = rw;
+      float arow[4][16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const float4 t = *reinterpret_cast<const float4*>(&sm.Ad[rw][qd + 4 * m][4 * j4]);
+          arow[m][4 * j4] = t.x; arow[m][4 * j4 + 1] = t.y;
+          arow[m][4 * j4 + 2] = t.z; arow[m][4 * j4 + 3] = t.w;
+        }
+      float x[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x[m] = (qd + 4 * m == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float xj = quad_bcast(x[j >> 2], j & 3);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = __builtin_fmaf(-arow[m][j], xj, x[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + 16 * bb + c], x[m]);
+    };
+    // all factors of chunk c (K/Q and gate buffer c % 3 -> factor buffer c & 1)
+    auto factors = [&](int c) {
+      const int kb = c % 3, ab = c & 1;
+      do_pair(rw, kb, ab, true);
+      do_pair(4 + rw, kb, ab, false);
+      if (rw < 2) do_pair(8 + rw, kb, ab, false);
+      invert_diag(ab);
+    };
+
+    load_kq(0);
+    if (rw == 0) load_gates(0);
+    stage_kq(0);
+    if (rw == 0) scan(0);
+    load_kq(1);
+    if (rw == 0) load_gates(1);
+    __syncthreads();
+    factors(0);
+    stage_kq(1);
+    if (rw == 0) scan(1);
+    load_kq(2);
+    if (rw == 0) load_gates(2);
+    __syncthreads();
+    for (int c = 0; c < nc; ++c) {
+      stage_kq((c + 2) % 3);
+      load_kq(c + 3);
+      if (rw == 0) {
+        scan(c + 2);
+        load_gates(c + 3);
+      }
+      factors(c + 1);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ================================================================== consumers
+  const int w = wave;
+  int v0[VB];
+#pragma unroll
+  for (int b = 0; b < VB; ++b) v0[b] = slice * DVS + 16 * (w * VB + b);
+
+  f32x4 st[VB][8];
+  float* const sbase = state + ((int64_t)s * Hv + h) * (DK * DK);
+  const bool init = has_init == nullptr || has_init[s] != 0;
+#pragma unroll
+  for (int b = 0; b < VB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      if (init) {
+        const float4 t = *reinterpret_cast<const float4*>(sbase + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg);
+        st[b][cb] = f32x4{t.x, t.y, t.z, t.w};
+      } else {
+        st[b][cb] = zero4();
+      }
+    }
+
+  if (nc > 0) {
+    // V of one chunk in the accumulator layout: lane holds tokens
+    // 16 ib + 4 kg + e of state row v0 + r16
+    uint16_t vr[VB][4][4];
+    auto load_v = [&](int c) {
+      const int64_t c0 = bos + BT * c;
+      const auto rv = buf_rsrc(v + c0 * Hv * DK, chunk_len(c) * Hv * DK * 2);
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vr[b][ib][e] = __builtin_amdgcn_raw_buffer_load_b16(
+                rv, (((16 * ib + 4 * kg + e) * Hv + h) * DK + v0[b] + r16) * 2, 0, 0);
+    };
+    // O of the previous chunk, packed, stored at the top of the next
+    // iteration: issued before that iteration's V loads, the stores are
+    // never inside a wait for loaded data (one in-order counter covers
+    // loads and stores)
+    u32x2 opk[VB][4];
+    __amdgpu_buffer_rsrc_t ro_prev = buf_rsrc(o, 0);
+    auto store_o = [&]() {
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int b = 0; b < VB; ++b)
+          __builtin_amdgcn_raw_buffer_store_b64(opk[b][ib], ro_prev,
+                                                (((16 * ib + r16) * Hv + h) * DK + v0[b] + 4 * kg) * 2, 0, 0);
+    };
+#pragma unroll
+    for (int b = 0; b < VB; ++b)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) opk[b][ib] = u32x2{0u, 0u};
+    load_v(0);
+    __syncthreads();
+    __syncthreads();
+
+    for (int c = 0; c < nc; ++c) {
+      const int n = chunk_len(c);
+      const int64_t c0 = bos + BT * c;
+      const int kb = c % 3, ab = c & 1;
+      const uint16_t* Kc = sm.K[kb];
+      const uint16_t* Qc = sm.Q[kb];
+      const uint16_t* ATc = sm.AT[ab];
+      const uint16_t* Pc = sm.P[ab];
+      const float* Wc = &sm.W[kb][0][0];
+      const float gamma_last = __builtin_amdgcn_exp2f(Wc[n - 1]);
+
+      float vv[VB][4][4];
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[b][ib][e] = bf16_to_f32(vr[b][ib][e]);
+      store_o();
+      load_v(c + 1);
+
+      // The chain of the chunk is Z -> R -> the four block steps of the
+      // solve -> the state update.  Each U block, once final, immediately
+      // feeds its share of the state update and of O, and the Q S0^T
+      // products are spread between the block steps, so the MFMA pipe has
+      // independent work while a block step waits on its predecessor.
+      // S0 is read as bf16 operands taken before the update (sb), so the
+      // float32 state is updated in place.
+
+      // gate vectors of this lane's rows (tokens 16 ib + 4 kg + e)
+      float gam4[4][4], b4[4][4], d4[4][4];
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const float4 ga = *reinterpret_cast<const float4*>(&Wc[BT + 16 * ib + 4 * kg]);
+        const float4 bt = *reinterpret_cast<const float4*>(&Wc[2 * BT + 16 * ib + 4 * kg]);
+        const float4 dd = *reinterpret_cast<const float4*>(&Wc[3 * BT + 16 * ib + 4 * kg]);
+        gam4[ib][0] = ga.x; gam4[ib][1] = ga.y; gam4[ib][2] = ga.z; gam4[ib][3] = ga.w;
+        b4[ib][0] = bt.x; b4[ib][1] = bt.y; b4[ib][2] = bt.z; b4[ib][3] = bt.w;
+        d4[ib][0] = dd.x; d4[ib][1] = dd.y; d4[ib][2] = dd.z; d4[ib][3] = dd.w;
+      }
+      typename PR::F32 sb[VB][4];
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sb[b][t] = PR::reg32(st[b][2 * t], st[b][2 * t + 1]);
+
+      // ---- Z = K S0^T (rows: tokens)
+      f32x4 z[VB][4];
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) z[b][ib] = zero4();
+      {
+        typename PR::F32 fk[2][4];
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) fk[0][ib] = kq_frag(Kc, 16 * ib + r16, 0, kg);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int cur = t & 1, nxt = cur ^ 1;
+          if (t < 3) {
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) fk[nxt][ib] = kq_frag(Kc, 16 * ib + r16, 32 * (t + 1), kg);
+          }
+#pragma unroll
+          for (int b = 0; b < VB; ++b)
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) z[b][ib] = PR::mma32(fk[cur][ib], sb[b][t], z[b][ib]);
+        }
+      }
+
+      // ---- R = diag(beta) (V - diag(gamma) Z)
+      f32x4 rr[VB][4];
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[b][ib][e] = b4[ib][e] * (vv[b][ib][e] - gam4[ib][e] * z[b][ib][e]);
+
+      // (Q S0^T)^T (rows: state rows, columns: tokens), one 32-wide slice
+      // of the contraction at a time
+      f32x4 qt[VB][4];
+#pragma unroll
+      for (int b = 0; b < VB; ++b)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) qt[b][ib] = zero4();
+      auto qs_step = [&](int t) {
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+          const auto fq = kq_frag(Qc, 16 * ib + r16, 32 * t, kg);
+#pragma unroll
+          for (int b = 0; b < VB; ++b) qt[b][ib] = PR::mma32(sb[b][t], fq, qt[b][ib]);
+        }
+      };
+      // S^T <- S^T + K^T diag(d) U over tokens kb .. kb+31 (the decay by
+      // gamma_last is applied with the first half)
+      auto state_half = [&](int kb, const typename PR::F32* du, bool first) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          const auto kt = kq_fragT(Kc, 16 * cb, kb, lane);
+#pragma unroll
+          for (int b = 0; b < VB; ++b) {
+            f32x4 acc = st[b][cb];
+            if (first) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[e] = gamma_last * acc[e];
+            }
+            st[b][cb] = PR::mma32(kt, du[b], acc);
+          }
+        }
+      };
+
+      // ---- block solve (I + A) U = R, interleaved with the products that
+      // each finished block enables.  An accumulator is never carried from
+      // a 16x16x32 MFMA into a 16x16x16 one: the hardware needs wait states
+      // between the two shapes that the compiler does not insert (the
+      // second one read stale accumulator elements), so mixed-shape sums are
+      // formed on separate accumulators and added.
+      f32x4 uu[VB][4], pu[VB][4];
+      {
+        const auto td = PR::lds16(ATc, LDT, r16, 0, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) uu[b][0] = PR::mma16(td, PR::reg16(rr[b][0]), zero4());
+      }
+      qs_step(0);
+      {
+        const auto am = PR::lds16(ATc, LDT, 16 + r16, 0, kg);
+        const auto td = PR::lds16(ATc, LDT, 16 + r16, 16, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          rr[b][1] = PR::mma16(am, PR::reg16(uu[b][0]), rr[b][1]);
+          uu[b][1] = PR::mma16(td, PR::reg16(rr[b][1]), zero4());
+        }
+      }
+      qs_step(1);
+      {
+        // blocks 0 and 1 are final: first half of the state update and
+        // their part of O
+        typename PR::F32 du[VB], u01[VB];
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          f32x4 d0, d1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d0[e] = uu[b][0][e] * d4[0][e];
+            d1[e] = uu[b][1][e] * d4[1][e];
+          }
+          du[b] = PR::reg32(d0, d1);
+          u01[b] = PR::reg32(uu[b][0], uu[b][1]);
+        }
+        const auto a2 = PR::lds32(ATc, LDT, 32 + r16, 0, kg);
+        const auto a3 = PR::lds32(ATc, LDT, 48 + r16, 0, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          rr[b][2] = PR::mma32(a2, u01[b], rr[b][2]);
+          rr[b][3] = PR::mma32(a3, u01[b], rr[b][3]);
+        }
+        const auto p0 = PR::lds16(Pc, LDT, r16, 0, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) pu[b][0] = PR::mma16(PR::reg16(uu[b][0]), p0, zero4());
+#pragma unroll
+        for (int ib = 1; ib < 4; ++ib) {
+          const auto p01 = PR::lds32(Pc, LDT, 16 * ib + r16, 0, kg);
+#pragma unroll
+          for (int b = 0; b < VB; ++b) pu[b][ib] = PR::mma32(u01[b], p01, zero4());
+        }
+        state_half(0, du, true);
+      }
+      {
+        const auto td = PR::lds16(ATc, LDT, 32 + r16, 32, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) uu[b][2] = PR::mma16(td, PR::reg16(rr[b][2]), zero4());
+      }
+      qs_step(2);
+      {
+        const auto am = PR::lds16(ATc, LDT, 48 + r16, 32, kg);
+        const auto td = PR::lds16(ATc, LDT, 48 + r16, 48, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          const f32x4 t3 = PR::mma16(am, PR::reg16(uu[b][2]), zero4());
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rr[b][3][e] += t3[e];
+          uu[b][3] = PR::mma16(td, PR::reg16(rr[b][3]), zero4());
+        }
+      }
+      qs_step(3);
+      {
+        // blocks 2 and 3: second half of the state update and the rest of O
+        typename PR::F32 du[VB], u23[VB];
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          f32x4 d2, d3;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d2[e] = uu[b][2][e] * d4[2][e];
+            d3[e] = uu[b][3][e] * d4[3][e];
+          }
+          du[b] = PR::reg32(d2, d3);
+          u23[b] = PR::reg32(uu[b][2], uu[b][3]);
+        }
+        state_half(32, du, false);
+        const auto p2 = PR::lds16(Pc, LDT, 32 + r16, 32, kg);
+        const auto p3 = PR::lds32(Pc, LDT, 48 + r16, 32, kg);
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          const f32x4 t2 = PR::mma16(PR::reg16(uu[b][2]), p2, zero4());
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pu[b][2][e] += t2[e];
+          pu[b][3] = PR::mma32(u23[b], p3, pu[b][3]);
+        }
+      }
+
+      // ---- O^T = (Q S0^T)^T diag(gamma) + U^T P^T; lane: token 16 ib + r16,
+      // state rows v0 + 4 kg .. +3
+      ro_prev = buf_rsrc(o + c0 * Hv * DK, n * Hv * DK * 2);
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const float gt = Wc[BT + 16 * ib + r16];
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          float ov[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = gt * qt[b][ib][e] + pu[b][ib][e];
+          opk[b][ib] = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+        }
+      }
+      __syncthreads();
+    }
+    store_o();
+  }
+
+#pragma unroll
+  for (int b = 0; b < VB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      *reinterpret_cast<float4*>(sbase + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg) =
+          make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
+}
+
+template <int VB>
+hipError_t launch_ws(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                     const int32_t* cu, int nseq, int Hk, int Hv, float* state,
+                     const uint8_t* has_init, void* o, hipStream_t st) {
+  const dim3 grid(nseq * Hv * (DK / (64 * VB)));
+  hipLaunchKernelGGL((prefill_ws_kernel<VB>), grid, dim3(512), 0, st, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta, cu, Hk,
+                     Hv, state, has_init, static_cast<uint16_t*>(o));
+  return hipGetLastError();
+}
+
 template <class T, int NW, int VB>
 hipError_t launch_t(const void* q, const void* k, const void* v, const float* g, const float* beta,
                     const int32_t* cu, int nseq, int Hk, int Hv, float* state,
@@ -578,13 +1171,10 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const float* g,
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int act, const float* g,
                           const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
                           float* state, const uint8_t* has_init, void* o, hipStream_t st) {
+  // float32 activations take the single-role schedule: three K/Q buffers of
+  // 4-byte elements do not fit in LDS.
   if (act == GDN_F32) return launch_t<float, 4, 1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
-  // Two 16-row blocks per wave (one workgroup per head) share every K / Q
-  // fragment between two MFMAs; with fewer than ~200 (sequence, head) units
-  // the chip is better filled by one block per wave (two workgroups per head).
-  if ((long long)nseq * Hv >= 192)
-    return launch_t<uint16_t, 4, 2>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
-  return launch_t<uint16_t, 4, 1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
+  return launch_ws<1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
 }
 
 }  // namespace gdn

@@ -244,6 +244,10 @@ REC_CASES = [
     ("bf16", I.GEO_TINY, [1, 2, 3, 63, 64, 65, 129, 200], [1, 0, 1, 0, 1, 1, 0, 1]),
     ("bf16", I.Geometry(Hk=1, Hv=3), [130, 7], [1, 0]),
     ("bf16", I.Geometry(Hk=2, Hv=2), [300], [1]),
+    # 6 sequences x 32 v-heads, lengths unsorted (longest-first dispatch)
+    ("bf16", I.GEO_8192, [1, 63, 65, 130, 200, 7], [1, 0, 1, 1, 0, 1]),
+    # more sequences than the longest-first ordering handles (kept in order)
+    ("bf16", I.GEO_TINY, [(7 * i) % 41 + 1 for i in range(70)], [i % 2 for i in range(70)]),
 ]
 
 
