@@ -1,18 +1,30 @@
 """GDN layer hot-path benchmark on one MI355X.
 
-One step = one pass of the whole hot path over one batch: exact conv chunks
-(device builder), causal conv with conv_state update, post-conv (SiLU,
-split, L2) and the chunked delta-rule prefill with the state update, on the
-bf16 varlen prefill workload (8 sequences with lengths uniform in
-[128, 2048], 8192 packed channels = 16 q + 16 k heads and 32 v heads of
-128, half of the sequences with initial states).  Inputs are synthetic and
-seeded, resident in HBM before timing starts.
+Default workload (the headline metric): the bf16 varlen prefill.  One step
+is one pass of the whole hot path over one batch: exact conv chunks (device
+builder), causal conv with the conv_state update, post-conv (SiLU, split,
+L2) and the chunked delta-rule prefill with the state update, on 8
+sequences with lengths uniform in [128, 2048], 8192 packed channels = 16 q
++ 16 k heads and 32 v heads of 128, half of the sequences with initial
+states.  Inputs are synthetic and seeded, resident in HBM before timing
+starts.
 
 Prints ONE JSON line: throughput in tokens/s, the roofline of the dominant
 kernel (per-launch HIP-event time of each kernel inside the timed region),
 and the CPU oracle timed on a bounded sample of the same workload.
 
+Other workloads (--workload), each one JSON line with per-kernel stages and
+the dominant kernel's roofline, throughput in layer-tokens/s:
+  verify  speculative verify: 36 layers of conv shift + post-conv + decode
+          step (no state write), then one batched commit of n_keep tokens
+          (32 sequences, 1..8 draft tokens each)
+  long    one 32768-token prefill layer
+  mixed   24 layers of a serving step: 8 prefill sequences (log-uniform
+          lengths in [256, 8192]) and 24 single-token decode sequences,
+          6144 channels (16 q, 16 k, 16 v heads)
+
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                  [--workload varlen|verify|long|mixed]
 """
 from __future__ import annotations
 
@@ -27,13 +39,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFS = 2500.0
 METRIC = "GDN layer tokens/s (conv+postconv+delta-rule) and % of HBM roofline, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_varlen_prefill_bf16.json")
 KERNEL_SOURCES = {
     "conv": ["conv.hip", "device_common.hpp"],
     "postconv": ["postconv.hip", "device_common.hpp"],
-    "prefill": ["prefill.hip", "device_common.hpp"],
+    "prefill": ["prefill.hip", "mfma.hpp", "device_common.hpp"],
+    "step": ["step.hip", "mfma.hpp", "device_common.hpp"],
+    "commit": ["step.hip", "mfma.hpp", "device_common.hpp"],
 }
+STATE_BYTES = 128 * 128 * 4   # one float32 state matrix (dv x dk)
 
 
 def source_hash(kernel: str) -> str:
@@ -44,21 +60,45 @@ def source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+# ------------------------------------------------------------ algorithmic bytes
+# Bytes each kernel must move at minimum (one launch).  e = activation bytes.
+
+def conv_bytes(N, C, e, n_init, nseq, write_state):
+    """x read, y written, weights (16 B) + bias slot (4 B) per channel, the
+    three float32 conv_state rows read for sequences with initial state and
+    written (when write_state) for every sequence."""
+    return 2 * N * C * e + 20 * C + n_init * 12 * C + (nseq * 12 * C if write_state else 0)
+
+
+def postconv_bytes(N, C, e):
+    return 2 * N * C * e
+
+
+def recurrence_bytes(N, Hk, Hv, e, n_state_read, n_state_write):
+    """q, k, v read, o written, g and beta read, plus whole float32 states."""
+    return (N * (2 * Hk * 128 + Hv * 128) * e + N * Hv * 8 + N * Hv * 128 * e
+            + (n_state_read + n_state_write) * Hv * STATE_BYTES)
+
+
+def commit_bytes(L, C, Hk, Hv, e, n_keep, nseq):
+    """Per layer, for each sequence that keeps n > 0 tokens: its state read
+    and written, the kept tokens' k, v, g, beta, and the conv_state rows
+    rebuilt from the kept x rows (12 B per channel read and written)."""
+    kept = sum(n_keep)
+    active = sum(1 for n in n_keep if n > 0)
+    per_layer = (active * Hv * 2 * STATE_BYTES + kept * (Hk * 128 + Hv * 128) * e + kept * Hv * 8
+                 + kept * C * e + active * 24 * C)
+    return L * per_layer
+
+
 def algorithmic_bytes(lb) -> dict:
-    """Bytes each kernel must move at minimum for this batch (per launch)."""
+    """Per-kernel bytes of the default varlen step (one launch each)."""
     N, C = lb.N, lb.geo.C
-    Hk, Hv = lb.geo.Hk, lb.geo.Hv
     e = 2 if lb.act == "bf16" else 4
     n_init = int(lb.has_init.sum())
-    nseq = lb.nseq
-    conv = 2 * N * C * e + 20 * C + n_init * 12 * C + nseq * 12 * C
-    post = N * C * e + N * C * e
-    state = Hv * 128 * 128 * 4
-    pre = (N * (2 * Hk * 128 + Hv * 128) * e      # q, k, v
-           + N * Hv * 8                            # g, beta
-           + N * Hv * 128 * e                      # o
-           + n_init * state + nseq * state)        # state read (if any) + write
-    return {"conv": conv, "postconv": post, "prefill": pre}
+    return {"conv": conv_bytes(N, C, e, n_init, lb.nseq, True),
+            "postconv": postconv_bytes(N, C, e),
+            "prefill": recurrence_bytes(N, lb.geo.Hk, lb.geo.Hv, e, n_init, lb.nseq)}
 
 
 def prefill_flops(lb) -> float:
@@ -103,11 +143,179 @@ def cpu_baseline(lb) -> dict:
             "seconds": round(dt, 2)}
 
 
+# ------------------------------------------------------------------ workloads
+# Each builder returns a plan: the ordered kernel launches of one step, the
+# algorithmic bytes per kernel name (summed over the step), the tokens of
+# one step and the config dict.
+
+class Plan:
+    def __init__(self):
+        self.launches = []       # (kernel name, callable)
+        self.bytes = {}          # kernel name -> bytes per step
+        self.count = {}          # kernel name -> launches per step
+        self.flops = {}          # kernel name -> dense flops per step
+        self.tokens = 0
+        self.config = {}
+        self.keep = []           # tensors kept alive
+
+    def add(self, name, fn, nbytes, flops=0.0):
+        self.launches.append((name, fn))
+        self.bytes[name] = self.bytes.get(name, 0) + nbytes
+        self.count[name] = self.count.get(name, 0) + 1
+        if flops:
+            self.flops[name] = self.flops.get(name, 0.0) + flops
+
+
+def _layer_on_device(lb, dev):
+    import torch
+    d = dict(x=lb.x.to(dev), w=lb.conv_w.to(dev), cs=lb.conv_state.to(dev), st=lb.state.to(dev),
+             g=lb.g.to(dev), beta=lb.beta.to(dev), cu=lb.cu_seqlens.to(dev),
+             hi=lb.has_init.to(dev))
+    N, C, Hk, Hv = lb.N, lb.geo.C, lb.geo.Hk, lb.geo.Hv
+    d["y"] = torch.empty(N, C, dtype=lb.x.dtype, device=dev)
+    d["q"] = torch.empty(N, Hk, 128, dtype=lb.x.dtype, device=dev)
+    d["k"] = torch.empty_like(d["q"])
+    d["v"] = torch.empty(N, Hv, 128, dtype=lb.x.dtype, device=dev)
+    d["o"] = torch.empty_like(d["v"])
+    return d
+
+
+def plan_varlen(dev):
+    import torch
+    from linear_attention_layers_amd import gdn, inputs
+    lb = inputs.varlen_prefill()
+    d = _layer_on_device(lb, dev)
+    Hk, Hv, N = lb.geo.Hk, lb.geo.Hv, lb.N
+    chunks = torch.empty(gdn.gdn_chunk_capacity(N, lb.nseq), 4, dtype=torch.int32, device=dev)
+    algo = algorithmic_bytes(lb)
+    p = Plan()
+    p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
+    p.add("conv", lambda: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], d["hi"], d["cu"],
+                                                  chunks, True, y=d["y"]), algo["conv"])
+    p.add("postconv", lambda: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"], k=d["k"], v=d["v"]),
+          algo["postconv"])
+    p.add("prefill", lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                        d["cu"], d["st"], d["hi"], o=d["o"]),
+          algo["prefill"], prefill_flops(lb))
+    p.tokens = N
+    p.config = {"workload": "varlen_prefill_bf16", "nseq": lb.nseq, "tokens": N,
+                "channels": lb.geo.C, "Hk": Hk, "Hv": Hv, "head_dim": 128, "layers": 1,
+                "state_dtype": "f32", "seed": 2000}
+    p.keep = [d, chunks]
+    p.lb = lb
+    return p
+
+
+def plan_verify(dev):
+    import torch
+    from linear_attention_layers_amd import gdn, inputs
+    L = 36
+    lengths, n_keep = inputs.spec_verify_window()
+    p = Plan()
+    table_layers = []
+    lb0 = None
+    for layer in range(L):
+        lb = inputs.spec_verify_layer(layer)
+        lb0 = lb0 or lb
+        d = _layer_on_device(lb, dev)
+        N, C, Hk, Hv = lb.N, lb.geo.C, lb.geo.Hk, lb.geo.Hv
+        chunks = gdn.gdn_make_chunks_device(d["cu"], N)
+        d["chunks"] = chunks
+        p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None, d["cu"],
+                                                         d["chunks"], False, y=d["y"]),
+              conv_bytes(N, C, 2, lb.nseq, lb.nseq, False))
+        p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"],
+                                                                         k=d["k"], v=d["v"]),
+              postconv_bytes(N, C, 2))
+        p.add("step", lambda d=d: gdn.gdn_delta_rule_step(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                          d["cu"], d["st"], None, o=d["o"],
+                                                          commit_state=False),
+              recurrence_bytes(N, Hk, Hv, 2, lb.nseq, 0))
+        p.keep.append(d)
+        table_layers.append(dict(x=d["x"], conv_state=d["cs"], state=d["st"], k=d["k"], v=d["v"],
+                                 g=d["g"], beta=d["beta"]))
+    table = gdn.gdn_layer_table(table_layers, dev)
+    cu0 = lb0.cu_seqlens.to(dev)
+    nk = lb0.n_keep.to(dev)
+    p.keep += [table, cu0, nk]
+    C, Hk, Hv = lb0.geo.C, lb0.geo.Hk, lb0.geo.Hv
+    p.add("commit", lambda: gdn.gdn_commit(table, L, cu0, nk, None, C, Hk, Hv, torch.bfloat16),
+          commit_bytes(L, C, Hk, Hv, 2, n_keep, len(lengths)))
+    p.tokens = L * sum(lengths)
+    p.config = {"workload": "spec_verify_36L_bf16", "nseq": len(lengths), "tokens": sum(lengths),
+                "kept_tokens": sum(n_keep), "channels": C, "Hk": Hk, "Hv": Hv, "head_dim": 128,
+                "layers": L, "state_dtype": "f32", "seed": 3000}
+    return p
+
+
+def plan_long(dev):
+    import torch
+    from linear_attention_layers_amd import gdn, inputs
+    lb = inputs.long_prefill()
+    d = _layer_on_device(lb, dev)
+    Hk, Hv, N, C = lb.geo.Hk, lb.geo.Hv, lb.N, lb.geo.C
+    chunks = torch.empty(gdn.gdn_chunk_capacity(N, lb.nseq), 4, dtype=torch.int32, device=dev)
+    p = Plan()
+    p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
+    p.add("conv", lambda: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], d["hi"], d["cu"],
+                                                  chunks, True, y=d["y"]), conv_bytes(N, C, 2, 0, 1, True))
+    p.add("postconv", lambda: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"], k=d["k"], v=d["v"]),
+          postconv_bytes(N, C, 2))
+    p.add("prefill", lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                        d["cu"], d["st"], d["hi"], o=d["o"]),
+          recurrence_bytes(N, Hk, Hv, 2, 0, 1), prefill_flops(lb))
+    p.tokens = N
+    p.config = {"workload": "long_prefill_32k_bf16", "nseq": 1, "tokens": N, "channels": C,
+                "Hk": Hk, "Hv": Hv, "head_dim": 128, "layers": 1, "state_dtype": "f32", "seed": 4000}
+    p.keep = [d, chunks]
+    return p
+
+
+def plan_mixed(dev):
+    from linear_attention_layers_amd import gdn, inputs
+    L = 24
+    p = Plan()
+    for layer in range(L):
+        lb = inputs.mixed_serving_layer(layer)
+        d = _layer_on_device(lb, dev)
+        npre = lb.meta["n_prefill"]
+        Npre = int(lb.cu_seqlens[npre])
+        N, C, Hk, Hv = lb.N, lb.geo.C, lb.geo.Hk, lb.geo.Hv
+        ndec = lb.nseq - npre
+        d["chunks"] = gdn.gdn_make_chunks_device(d["cu"], N)
+        d["cu_pre"] = d["cu"][:npre + 1]
+        d["cu_dec"] = (d["cu"][npre:] - Npre).contiguous()
+        p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None, d["cu"],
+                                                         d["chunks"], True, y=d["y"]),
+              conv_bytes(N, C, 2, lb.nseq, lb.nseq, True))
+        p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"],
+                                                                         k=d["k"], v=d["v"]),
+              postconv_bytes(N, C, 2))
+        p.add("prefill", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_prefill(
+                  d["q"][:n], d["k"][:n], d["v"][:n], d["g"][:n], d["beta"][:n], d["cu_pre"],
+                  d["st"][:m], None, o=d["o"][:n]),
+              recurrence_bytes(Npre, Hk, Hv, 2, npre, npre), 11.0 * 128 * 128 * Npre * Hv)
+        p.add("step", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_step(
+                  d["q"][n:], d["k"][n:], d["v"][n:], d["g"][n:], d["beta"][n:], d["cu_dec"],
+                  d["st"][m:], None, o=d["o"][n:], commit_state=True),
+              recurrence_bytes(N - Npre, Hk, Hv, 2, ndec, ndec))
+        p.keep.append(d)
+        p.tokens += N
+        p.config = {"workload": "mixed_serving_24L_bf16", "prefill_seqs": npre, "decode_seqs": ndec,
+                    "tokens_per_layer": N, "channels": C, "Hk": Hk, "Hv": Hv, "head_dim": 128,
+                    "layers": L, "state_dtype": "f32", "seed": 5000}
+    return p
+
+
+PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", choices=sorted(PLANS), default="varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
@@ -118,6 +326,9 @@ def main():
               "(the GDN hot path shards by sequence and head group with no exchange; "
               "multi-GPU runs are not part of this build)", file=sys.stderr)
         sys.exit(2)
+    default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 10}[args.workload]
+    steps = args.steps if args.steps is not None else default_steps
+    warmup = args.warmup if args.warmup is not None else max(2, steps // 10)
 
     import torch
 
@@ -134,107 +345,89 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
         return
 
-    from linear_attention_layers_amd import gdn, inputs
-
-    lb = inputs.varlen_prefill()
-    Hk, Hv, C, N = lb.geo.Hk, lb.geo.Hv, lb.geo.C, lb.N
-    x = lb.x.to(dev)
-    w = lb.conv_w.to(dev)
-    cs = lb.conv_state.to(dev)
-    st = lb.state.to(dev)
-    g = lb.g.to(dev)
-    beta = lb.beta.to(dev)
-    cu = lb.cu_seqlens.to(dev)
-    hi = lb.has_init.to(dev)
-    cap = gdn.gdn_chunk_capacity(N, lb.nseq)
-    chunks = torch.empty(cap, 4, dtype=torch.int32, device=dev)
-    y = torch.empty(N, C, dtype=torch.bfloat16, device=dev)
-    q = torch.empty(N, Hk, 128, dtype=torch.bfloat16, device=dev)
-    k = torch.empty_like(q)
-    v = torch.empty(N, Hv, 128, dtype=torch.bfloat16, device=dev)
-    o = torch.empty_like(v)
+    plan = PLANS[args.workload](dev)
     stream = torch.cuda.current_stream()
-
-    names = ["chunks", "conv", "postconv", "prefill"]
+    n_l = len(plan.launches)
 
     def step(ev=None):
-        def mark(i):
+        if ev is not None:
+            ev[0].record(stream)
+        for i, (_, fn) in enumerate(plan.launches):
+            fn()
             if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        gdn.gdn_make_chunks_device(cu, N, out=chunks)
-        mark(1)
-        gdn.gdn_causal_conv_fwd(x, w, None, cs, hi, cu, chunks, True, y=y)
-        mark(2)
-        gdn.gdn_postconv_l2(y, Hk, Hv, 1e-6, q=q, k=k, v=v)
-        mark(3)
-        gdn.gdn_delta_rule_prefill(q, k, v, g, beta, cu, st, hi, o=o)
-        mark(4)
+                ev[i + 1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_l + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_kernel_ms = {nm: 0.0 for nm in names}
+    names = list(dict.fromkeys(nm for nm, _ in plan.launches))
+    per_step_ms = {nm: 0.0 for nm in names}
     for ev in events:
-        for j, nm in enumerate(names):
-            per_kernel_ms[nm] += ev[j].elapsed_time(ev[j + 1])
-    per_kernel_ms = {nm: t / args.steps for nm, t in per_kernel_ms.items()}
+        for j, (nm, _) in enumerate(plan.launches):
+            per_step_ms[nm] += ev[j].elapsed_time(ev[j + 1])
+    per_step_ms = {nm: t / steps for nm, t in per_step_ms.items()}
 
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_s = N / (ms_per_step / 1e3)
-    algo = algorithmic_bytes(lb)
+    ms_per_step = wall * 1e3 / steps
+    tokens_per_s = plan.tokens / (ms_per_step / 1e3)
     stages = {}
-    for nm in ("conv", "postconv", "prefill"):
-        t = per_kernel_ms[nm] / 1e3
-        stages[nm] = {"us": round(per_kernel_ms[nm] * 1e3, 2),
-                      "GB/s": round(algo[nm] / t / 1e9, 1),
-                      "hbm_frac": round(algo[nm] / t / 1e9 / HBM_PEAK_GBS, 4)}
-    stages["prefill"]["mfma_TFLOP/s"] = round(prefill_flops(lb) / (per_kernel_ms["prefill"] / 1e3) / 1e12, 2)
-    stages["chunks"] = {"us": round(per_kernel_ms["chunks"] * 1e3, 2)}
-    dominant = max(("conv", "postconv", "prefill"), key=lambda nm: per_kernel_ms[nm])
-    achieved = algo[dominant] / (per_kernel_ms[dominant] / 1e3) / 1e9
+    for nm in names:
+        t = per_step_ms[nm] / 1e3
+        rec = {"us_per_launch": round(per_step_ms[nm] * 1e3 / plan.count[nm], 2),
+               "launches": plan.count[nm]}
+        if plan.bytes.get(nm):
+            rec["GB/s"] = round(plan.bytes[nm] / t / 1e9, 1)
+            rec["hbm_frac"] = round(plan.bytes[nm] / t / 1e9 / HBM_PEAK_GBS, 4)
+        if plan.flops.get(nm):
+            tf = plan.flops[nm] / t / 1e12
+            rec["mfma_TFLOP/s"] = round(tf, 2)
+            rec["mfma_frac_bf16_dense"] = round(tf / BF16_MFMA_PEAK_TFS, 4)
+        stages[nm] = rec
+    timed = [nm for nm in names if plan.bytes.get(nm)]
+    dominant = max(timed, key=lambda nm: per_step_ms[nm])
+    achieved = plan.bytes[dominant] / (per_step_ms[dominant] / 1e3) / 1e9
 
     traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(dominant)
-        if rec and rec.get("source_hash") == source_hash(dominant):
-            traffic = rec["bytes_per_launch"]
-    except (OSError, ValueError):
-        pass
+    if args.workload == "varlen":
+        try:
+            with open(TRAFFIC_FILE) as f:
+                rec = json.load(f).get(dominant)
+            if rec and rec.get("source_hash") == source_hash(dominant):
+                traffic = rec["bytes_per_launch"]
+        except (OSError, ValueError):
+            pass
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "varlen" else
+        f"GDN {args.workload} step layer-tokens/s and % of HBM roofline, 1 GPU",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "varlen_prefill_bf16", "nseq": lb.nseq, "tokens": N,
-                   "channels": C, "Hk": Hk, "Hv": Hv, "head_dim": 128, "layers": 1,
-                   "state_dtype": "f32", "seed": 2000},
+        "config": plan.config,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": algo[dominant]},
+                     "traffic": traffic,
+                     "algorithmic_bytes": plan.bytes[dominant] // plan.count[dominant]},
         "stages": stages,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(lb)
+    if args.workload == "varlen" and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(plan.lb)
     print(json.dumps(out), flush=True)
 
 

@@ -40,8 +40,8 @@
 // rounded to bf16 only as an MFMA operand; the 16x16 diagonal inverses are
 // float32.  float32 activations: every contraction uses
 // v_mfma_f32_16x16x4_f32 on float32 operands.
-#include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace gdn {
 
@@ -51,142 +51,6 @@ constexpr int BT = 64;    // chunk length
 constexpr int DK = 128;   // head size
 constexpr float kLog2e = 1.4426950408889634f;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// ------------------------------------------------------------ MFMA operands
-// A 16 x 16 (rows x contraction) fragment: lane (r, kg) = (lane % 16,
-// lane / 16) holds contraction slots 4kg .. 4kg+3 of row r.  A 16 x 32
-// fragment holds slots 4kg..4kg+3 of the first 16 and then of the second 16.
-// Every operand uses this slot order, and an accumulator tile's rows
-// 4kg..4kg+3 are a lane's slots, so tiles feed the B side directly.
-template <class T> struct Prec;
-
-template <> struct Prec<uint16_t> {
-  using E = uint16_t;
-  static constexpr int PAD = 8;
-  struct F16 { uint2 v; };
-  struct F32 { uint4 v; };
-  // row-major LDS matrix, fragment of rows row0.., contraction kb..
-  __device__ __forceinline__ static F16 lds16(const E* p, int ld, int row, int kb, int kg) {
-    F16 f;
-    f.v = *reinterpret_cast<const uint2*>(p + row * ld + kb + 4 * kg);
-    return f;
-  }
-  __device__ __forceinline__ static F32 lds32(const E* p, int ld, int row, int kb, int kg) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p + row * ld + kb + 4 * kg);
-    const uint2 b = *reinterpret_cast<const uint2*>(p + row * ld + kb + 16 + 4 * kg);
-    F32 f;
-    f.v = make_uint4(a.x, a.y, b.x, b.y);
-    return f;
-  }
-  // Transposed fragment of a row-major LDS matrix M: rows = M's columns
-  // c0..c0+15, contraction = M's rows kb..kb+31.  In each 16-lane group the
-  // transposing load hands lane r, slot j the element loaded by lane
-  // 4j + r/4 at slot r%4, so lane s of group kg loads M[kb + 4kg + s/4]
-  // [c0 + 4 (s%4) .. +3].
-  __device__ __forceinline__ static F32 ldsT32(const E* p, int ld, int c0, int kb, int lane) {
-    const int s = lane & 15, kg = lane >> 4;
-    const E* a = p + (kb + 4 * kg + (s >> 2)) * ld + c0 + 4 * (s & 3);
-    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
-    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 16 * ld));
-    const uint2 ux = __builtin_bit_cast(uint2, x), uy = __builtin_bit_cast(uint2, y);
-    F32 f;
-    f.v = make_uint4(ux.x, ux.y, uy.x, uy.y);
-    return f;
-  }
-  __device__ __forceinline__ static F16 reg16(f32x4 d) {
-    F16 f;
-    f.v = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
-    return f;
-  }
-  __device__ __forceinline__ static F32 reg32(f32x4 d0, f32x4 d1) {
-    F32 f;
-    f.v = make_uint4(pack_bf16x2(d0[0], d0[1]), pack_bf16x2(d0[2], d0[3]), pack_bf16x2(d1[0], d1[1]),
-                     pack_bf16x2(d1[2], d1[3]));
-    return f;
-  }
-  __device__ __forceinline__ static f32x4 mma16(F16 a, F16 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v),
-                                                     __builtin_bit_cast(s16x4, b.v), c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static f32x4 mma32(F32 a, F32 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
-                                                    __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
-  }
-  __device__ __forceinline__ static void put(E* p, float x) { *p = static_cast<E>(f32_to_bf16(x)); }
-  // 8 consecutive activations in storage form (one 16-byte piece)
-  struct Raw8 { uint4 v; };
-  __device__ __forceinline__ static Raw8 load_raw8(const uint16_t* p) {
-    Raw8 r;
-    r.v = *reinterpret_cast<const uint4*>(p);
-    return r;
-  }
-  __device__ __forceinline__ static Raw8 zero_raw8() { Raw8 r; r.v = make_uint4(0, 0, 0, 0); return r; }
-  __device__ __forceinline__ static void store_raw8(E* p, Raw8 r) { *reinterpret_cast<uint4*>(p) = r.v; }
-  __device__ __forceinline__ static float to_f32(E x) { return bf16_to_f32(x); }
-};
-
-template <> struct Prec<float> {
-  using E = float;
-  static constexpr int PAD = 4;
-  struct F16 { f32x4 v; };
-  struct F32 { f32x4 a, b; };
-  __device__ __forceinline__ static F16 lds16(const E* p, int ld, int row, int kb, int kg) {
-    F16 f;
-    const float4 t = *reinterpret_cast<const float4*>(p + row * ld + kb + 4 * kg);
-    f.v = f32x4{t.x, t.y, t.z, t.w};
-    return f;
-  }
-  __device__ __forceinline__ static F32 lds32(const E* p, int ld, int row, int kb, int kg) {
-    F32 f;
-    f.a = lds16(p, ld, row, kb, kg).v;
-    f.b = lds16(p, ld, row, kb + 16, kg).v;
-    return f;
-  }
-  __device__ __forceinline__ static F32 ldsT32(const E* p, int ld, int c0, int kb, int lane) {
-    const int r = lane & 15, kg = lane >> 4;
-    F32 f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f.a[t] = p[(kb + 4 * kg + t) * ld + c0 + r];
-      f.b[t] = p[(kb + 16 + 4 * kg + t) * ld + c0 + r];
-    }
-    return f;
-  }
-  __device__ __forceinline__ static F16 reg16(f32x4 d) { F16 f; f.v = d; return f; }
-  __device__ __forceinline__ static F32 reg32(f32x4 d0, f32x4 d1) { F32 f; f.a = d0; f.b = d1; return f; }
-  // slot t of lane kg is contraction index 4kg + t: four k = 4 steps
-  __device__ __forceinline__ static f32x4 mma4x(f32x4 a, f32x4 b, f32x4 c) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], c, 0, 0, 0);
-    return c;
-  }
-  __device__ __forceinline__ static f32x4 mma16(F16 a, F16 b, f32x4 c) { return mma4x(a.v, b.v, c); }
-  __device__ __forceinline__ static f32x4 mma32(F32 a, F32 b, f32x4 c) {
-    c = mma4x(a.a, b.a, c);
-    return mma4x(a.b, b.b, c);
-  }
-  __device__ __forceinline__ static void put(E* p, float x) { *p = x; }
-  struct Raw8 { float4 a, b; };
-  __device__ __forceinline__ static Raw8 load_raw8(const float* p) {
-    Raw8 r;
-    r.a = *reinterpret_cast<const float4*>(p);
-    r.b = *reinterpret_cast<const float4*>(p + 4);
-    return r;
-  }
-  __device__ __forceinline__ static Raw8 zero_raw8() {
-    Raw8 r;
-    r.a = make_float4(0.f, 0.f, 0.f, 0.f);
-    r.b = r.a;
-    return r;
-  }
-  __device__ __forceinline__ static void store_raw8(E* p, Raw8 r) {
-    *reinterpret_cast<float4*>(p) = r.a;
-    *reinterpret_cast<float4*>(p + 4) = r.b;
-  }
-  __device__ __forceinline__ static float to_f32(E x) { return x; }
-};
 
 template <class T, int NW> struct __attribute__((aligned(16))) Smem {
   using E = typename Prec<T>::E;
@@ -199,38 +63,6 @@ template <class T, int NW> struct __attribute__((aligned(16))) Smem {
   float Ad[4][16][20];  // diagonal 16x16 blocks of A, row-major (rows 16-byte aligned)
   float W[NW][4][BT];   // per-wave copies of log2-scaled G, gamma, beta, d
 };
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Value of lane `src` (0..3, a constant) of each DPP quad, in all four lanes.
-__device__ __forceinline__ float quad_bcast(float v, int src) {
-  switch (src) {
-    case 0: return dpp_mov<0x00>(v);
-    case 1: return dpp_mov<0x55>(v);
-    case 2: return dpp_mov<0xAA>(v);
-    default: return dpp_mov<0xFF>(v);
-  }
-}
-
-// v moved by a DPP control; lanes without a source (or outside row_mask)
-// read 0.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_or_zero(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
-}
-
-// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
-// 16-lane row, then the rows' totals are carried forward with row_bcast:15
-// and row_bcast:31.
-__device__ __forceinline__ float wave_prefix_sum(float v) {
-  v += dpp_or_zero<0x111, 0xf>(v);
-  v += dpp_or_zero<0x112, 0xf>(v);
-  v += dpp_or_zero<0x114, 0xf>(v);
-  v += dpp_or_zero<0x118, 0xf>(v);
-  v += dpp_or_zero<0x142, 0xa>(v);
-  v += dpp_or_zero<0x143, 0xc>(v);
-  return v;
-}
 
 // The 10 lower 16x16 tile pairs (bi, bj): the four diagonal ones first.
 __device__ __forceinline__ void tile_pair(int p, int& bi, int& bj) {
@@ -584,18 +416,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(
 // The pair products are formed transposed for the same reason: each lane
 // writes four consecutive columns of P and -A.
 
-constexpr int kBufDword3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kOrderMax = 64;            // batches up to this size run longest first
-
-// The size is made wave-uniform explicitly so the descriptor lives in
-// scalar registers (a vector-register descriptor costs a waterfall loop).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, __builtin_amdgcn_readfirstlane(bytes),
-                                           kBufDword3);
-}
-
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // K and Q tiles (64 tokens x 128 features, bf16) are stored unpadded with
 // the 8-byte granules of row r XOR-permuted by sig(r) = 4 (r % 8) +

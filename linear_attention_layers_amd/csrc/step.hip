@@ -8,141 +8,334 @@
 // two are bitwise equal ("Summary" item 1); all layers commit in one launch
 // instead of one launch per layer.
 //
-// Recurrence (gated delta rule), per row i of the dv x dk state S:
-//   u_i = S_i . k,   w_i = S_i . q,   kq = k . q
-//   d_i = b (v_i - a u_i)
-//   S_i <- a S_i + d_i k          (= a S_i (I - b k k^T) + b v_i k^T)
-//   o_i  = a w_i + d_i kq         (= S_i q after the update)
+// Recurrence (gated delta rule), per token t of a sequence's window, with
+// the dv x dk state S:
+//   u = S k_t,   d_t = b_t (v_t - a_t u),   S <- a_t S + d_t k_t^T,
+//   o_t = S q_t  (after the update).
 //
-// Layout: one workgroup of 256 lanes per (sequence, v-head).  Lane (rg, cl)
-// = (tid / 16, tid % 16) holds rows rg + 16 r (r = 0..7) and columns
-// 8 cl .. 8 cl + 7 of S in 64 registers, loaded once with 16-byte accesses
-// (16 lanes cover one 512-byte row).  Each token needs the 17 row dot
-// products above; each is 8 in-lane FMAs and a 16-lane DPP reduction in the
-// fixed xor order, so the state never leaves registers between tokens and
-// there is no barrier in the token loop.  All arithmetic in the update is
-// written as explicit fmaf / mul so the step and the commit replay (the same
-// function) are bitwise identical.
-#include "device_common.hpp"
+// Evaluation.  The window is taken 16 tokens at a time.  Unrolling the
+// recurrence over a block of n <= 16 tokens that enters with state S0, with
+// L_t = sum_{s<=t} log a_s and gamma_t = exp(L_t):
+//   the deltas d_t solve (I + A) D = R, A_ts = b_t exp(L_t - L_s) (k_t . k_s)
+//   for s < t, R_t = b_t (v_t - gamma_t S0 k_t);
+//   o_t = gamma_t S0 q_t + sum_{s<=t} exp(L_t - L_s) (q_t . k_s) d_s;
+//   S_n = gamma_{n-1} S0 + sum_s exp(L_{n-1} - L_s) d_s k_s^T.
+// Row t of D is exactly the per-token delta of token t, so this is the
+// per-token recurrence reassociated: S0 is read once per block, the
+// products S0 K^T, S0 Q^T, K K^T, Q K^T and the state update run on MFMA,
+// and the n-step dependency between tokens is one 16x16 unit-lower-
+// triangular inverse.  The kernel is then bound by reading (and, when
+// committing, writing) the float32 state.
+//
+// Layout.  One workgroup of 4 waves per (sequence, v-head); wave w owns
+// state rows 32 w .. 32 w + 31 as two 16-row blocks, held TRANSPOSED in
+// MFMA accumulators (the prefill's layout).  Every wave loads the block's K
+// and Q fragments itself and keeps its own LDS scratch, so there is no
+// barrier.  The commit replays the kept tokens through the same function,
+// so its state is bitwise equal to the state a committing step over those
+// tokens writes.
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace gdn {
 
 namespace {
 
 constexpr int kStepThreads = 256;
+constexpr int kWin = 16;     // tokens per block of a window
+constexpr float kLog2e = 1.4426950408889634f;
 
-struct StateRegs {
-  float s[8][8];  // [row r][column j]
+template <class T> struct StepSmem {
+  using E = typename Prec<T>::E;
+  static constexpr int LDK = 128 + Prec<T>::PAD;   // K rows of the block
+  static constexpr int LDT = kWin + Prec<T>::PAD;  // rows of T = (I + A)^-1
+  E K[4][kWin * LDK];
+  E Tm[4][kWin * LDT];
+  float A[4][kWin][20];
+  float W[4][4][64];        // log2-scaled L, gamma, beta, d of the block's tokens (entries
+                            // past 16 are written by the other lanes and never read)
 };
 
-__device__ __forceinline__ void load_state(const float* __restrict__ base, int rg, int cl,
-                                           StateRegs& S) {
+// S^T of rows v0 + 16 b + r16 in accumulator layout: tile cb holds
+// S[v0 + 16 b + r16][16 cb + 4 kg + e].  Read through a buffer resource
+// that spans the state, or nothing (all zeros) when there is no initial
+// state, so the read is branch-free.
+__device__ __forceinline__ void load_state(const float* base, bool init, int v0, int r16, int kg,
+                                           f32x4 (&st)[2][8]) {
+  const auto rs = buf_rsrc(base, init ? 128 * 128 * 4 : 0);
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const float* p = base + (rg + 16 * r) * 128 + 8 * cl;
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    S.s[r][0] = a.x; S.s[r][1] = a.y; S.s[r][2] = a.z; S.s[r][3] = a.w;
-    S.s[r][4] = b.x; S.s[r][5] = b.y; S.s[r][6] = b.z; S.s[r][7] = b.w;
-  }
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      st[b][cb] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((v0 + 16 * b + r16) * 128 + 16 * cb + 4 * kg) * 4, 0, 0));
 }
 
-__device__ __forceinline__ void store_state(float* __restrict__ base, int rg, int cl,
-                                            const StateRegs& S) {
+__device__ __forceinline__ void store_state(float* base, int v0, int r16, int kg, const f32x4 (&st)[2][8]) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    float* p = base + (rg + 16 * r) * 128 + 8 * cl;
-    *reinterpret_cast<float4*>(p) = make_float4(S.s[r][0], S.s[r][1], S.s[r][2], S.s[r][3]);
-    *reinterpret_cast<float4*>(p + 4) = make_float4(S.s[r][4], S.s[r][5], S.s[r][6], S.s[r][7]);
-  }
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      *reinterpret_cast<float4*>(base + (v0 + 16 * b + r16) * 128 + 16 * cb + 4 * kg) =
+          make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
 }
 
-// Runs tokens [t_begin, t_end) of one (sequence, v-head) through the state
-// held in S.  When WRITE_O, o[t][h][row] is written by lane cl == r.
-template <class T, bool WRITE_O>
-__device__ __forceinline__ void run_tokens(StateRegs& S, const T* __restrict__ q,
-                                           const T* __restrict__ k, const T* __restrict__ v,
-                                           const float* __restrict__ g,
-                                           const float* __restrict__ beta, T* __restrict__ o,
-                                           int t_begin, int t_end, int Hk, int Hv, int h, int kh,
-                                           int rg, int cl) {
-#pragma clang fp contract(off)
-  for (int t = t_begin; t < t_end; ++t) {
-    float kv[8], qv[8];
-    Act<T>::load8(k + ((int64_t)t * Hk + kh) * 128 + 8 * cl, kv);
-    if (WRITE_O) {
-      Act<T>::load8(q + ((int64_t)t * Hk + kh) * 128 + 8 * cl, qv);
+// Token inputs of one block of a window, in registers.
+template <class T, bool WITH_O> struct BlockIn {
+  typename Prec<T>::F32 kf[4], qf[4];   // K, Q fragments (token r16)
+  float vv[2][4];                       // V (token 4 kg + e, state row v0 + 16 b + r16)
+  float gl, bl;                         // log a, beta of token `lane` (lanes < 16)
+  int n;
+  int64_t t0;
+};
+
+template <class T, bool WITH_O>
+__device__ __forceinline__ void load_block(BlockIn<T, WITH_O>& in, int lane, const T* q, const T* k,
+                                           const T* v, const float* g, const float* beta, int64_t t0,
+                                           int n, int Hk, int Hv, int h, int kh, int v0) {
+  using PR = Prec<T>;
+  constexpr int ES = sizeof(typename PR::E);
+  const int r16 = lane & 15, kg = lane >> 4;
+  in.n = n;
+  in.t0 = t0;
+  const auto rg = buf_rsrc(g + t0 * Hv, n * Hv * 4);
+  const auto rb = buf_rsrc(beta + t0 * Hv, n * Hv * 4);
+  const int goff = ((lane & 15) * Hv + h) * 4;
+  in.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
+  in.bl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, goff, 0, 0));
+  const auto rk = buf_rsrc(k + t0 * Hk * 128, n * Hk * 128 * ES);
+  const auto rq = buf_rsrc(q + t0 * Hk * 128, n * Hk * 128 * ES);
+  const auto rv = buf_rsrc(v + t0 * Hv * 128, n * Hv * 128 * ES);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int off = ((r16 * Hk + kh) * 128 + 32 * t + 4 * kg) * ES;
+    in.kf[t] = PR::gfrag32(rk, off);
+    if (WITH_O) in.qf[t] = PR::gfrag32(rq, off);
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) in.vv[b][e] = PR::gload1(rv, (((4 * kg + e) * Hv + h) * 128 + v0 + 16 * b + r16) * ES);
+}
+
+// One block of a window: o of its tokens (WITH_O) and, when `advance`, the
+// state moved past them.
+template <class T, bool WITH_O>
+__device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f32x4 (&st)[2][8],
+                                          const BlockIn<T, WITH_O>& in, T* o, int Hv, int h,
+                                          bool advance) {
+  using PR = Prec<T>;
+  using E = typename PR::E;
+  constexpr int ES = sizeof(E);
+  constexpr int LDK = StepSmem<T>::LDK, LDT = StepSmem<T>::LDT;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int v0 = 32 * wave;
+  const int n = in.n;
+  E* Ks = sm.K[wave];
+  E* Tm = sm.Tm[wave];
+  float* Wl = &sm.W[wave][0][0];
+
+  // gate vectors: lane t < 16 holds token t (zero past the block's end);
+  // every lane writes its slot, so the loads are never sunk into a branch
+  {
+    const float gl = lane < kWin ? in.gl : 0.f;
+    const float L = wave_prefix_sum(gl) * kLog2e;
+    const float Llast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), n - 1));
+    Wl[lane] = L;
+    Wl[64 + lane] = __builtin_amdgcn_exp2f(L);
+    Wl[128 + lane] = in.bl;
+    Wl[192 + lane] = lane < n ? __builtin_amdgcn_exp2f(Llast - L) : 0.f;
+  }
+
+  // this wave's copy of the block's K rows, for the transposed read
+#pragma unroll
+  for (int t = 0; t < 4; ++t) PR::put_frag32(Ks + r16 * LDK + 32 * t + 4 * kg, in.kf[t]);
+
+  // transposed token products: lane (r16, kg) element e holds k_j . k_i
+  // and k_j . q_i for i = r16, j = 4 kg + e
+  f32x4 kk = zero4(), qk = zero4();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    kk = PR::mma32(in.kf[t], in.kf[t], kk);
+    if (WITH_O) qk = PR::mma32(in.kf[t], in.qf[t], qk);
+  }
+
+  // A (row i = r16, columns j = 4 kg + e) to LDS, P kept as the B operand
+  // of U^T P^T
+  float pv[4];
+  {
+    const float Li = Wl[r16], bi = Wl[128 + r16];
+    const float4 Lj = *reinterpret_cast<const float4*>(&Wl[4 * kg]);
+    const float lj[4] = {Lj.x, Lj.y, Lj.z, Lj.w};
+    float av[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * kg + e;
+      const float dec = j <= r16 ? __builtin_amdgcn_exp2f(Li - lj[e]) : 0.f;
+      av[e] = j < r16 ? bi * dec * kk[e] : 0.f;
+      pv[e] = dec * qk[e];
     }
-    float vr[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) vr[r] = Act<T>::load1(v + ((int64_t)t * Hv + h) * 128 + rg + 16 * r);
-    const float a = expf(g[(int64_t)t * Hv + h]);
-    const float b = beta[(int64_t)t * Hv + h];
+    *reinterpret_cast<float4*>(&sm.A[wave][r16][4 * kg]) = make_float4(av[0], av[1], av[2], av[3]);
+  }
 
-    float u[8], w[8];
+  // T = (I + A)^-1 by forward substitution: lane (c, q) = (lane / 4,
+  // lane % 4) owns rows q, q+4, q+8, q+12 of column c; the four lanes of a
+  // column form a DPP quad and x_j, once final, is broadcast from the lane
+  // owning row j.  Terms with j >= i vanish: A is strictly lower
+  // triangular.
+  {
+    const int c = lane >> 2, qd = lane & 3;
+    float x[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float pu = S.s[r][0] * kv[0];
+    for (int m = 0; m < 4; ++m) x[m] = (qd + 4 * m == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 1; j < 8; ++j) pu = __builtin_fmaf(S.s[r][j], kv[j], pu);
-      u[r] = pu;
-      if (WRITE_O) {
-        float pw = S.s[r][0] * qv[0];
+    for (int j4 = 0; j4 < 4; ++j4) {
+      float a4[4][4];   // A[qd + 4 m][4 j4 .. 4 j4 + 3]
 #pragma unroll
-        for (int j = 1; j < 8; ++j) pw = __builtin_fmaf(S.s[r][j], qv[j], pw);
-        w[r] = pw;
+      for (int m = 0; m < 4; ++m) {
+        const float4 t = *reinterpret_cast<const float4*>(&sm.A[wave][qd + 4 * m][4 * j4]);
+        a4[m][0] = t.x; a4[m][1] = t.y; a4[m][2] = t.z; a4[m][3] = t.w;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float xj = quad_bcast(x[j4], jj);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = __builtin_fmaf(-a4[m][jj], xj, x[m]);
       }
     }
-    float kq = 0.f;
-    if (WRITE_O) {
-      float p = kv[0] * qv[0];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) p = __builtin_fmaf(kv[j], qv[j], p);
-      kq = row16_sum(p);
+    for (int m = 0; m < 4; ++m) PR::put(&Tm[(qd + 4 * m) * LDT + c], x[m]);
+  }
+  const auto tf = PR::lds16(Tm, LDT, r16, 0, kg);
+
+  // Z = K S0^T (rows: tokens) and (Q S0^T)^T (rows: state rows)
+  f32x4 z[2], qt[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) { z[b] = zero4(); qt[b] = zero4(); }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const auto bs = PR::reg32(st[b][2 * t], st[b][2 * t + 1]);
+      z[b] = PR::mma32(in.kf[t], bs, z[b]);
+      if (WITH_O) qt[b] = PR::mma32(bs, in.qf[t], qt[b]);
+    }
+
+  // R = diag(beta) (V - diag(gamma) Z), D = T R (rows: tokens)
+  const float4 ga = *reinterpret_cast<const float4*>(&Wl[64 + 4 * kg]);
+  const float4 be = *reinterpret_cast<const float4*>(&Wl[128 + 4 * kg]);
+  const float4 dd = *reinterpret_cast<const float4*>(&Wl[192 + 4 * kg]);
+  const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
+  const float dec4[4] = {dd.x, dd.y, dd.z, dd.w};
+  f32x4 dl[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    f32x4 rr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rr[e] = bet[e] * (in.vv[b][e] - gam[e] * z[b][e]);
+    dl[b] = PR::mma16(tf, PR::reg16(rr), zero4());
+  }
+
+  // O^T = (Q S0^T)^T diag(gamma) + D^T P^T; lane: token r16, state rows
+  // v0 + 16 b + 4 kg .. +3.  The 16-wide product is formed on its own
+  // accumulator: an accumulator is never carried from a 16x16x32 MFMA into
+  // a 16x16x16 one (the hardware needs wait states between the two shapes
+  // that the compiler does not insert).
+  if (WITH_O) {
+    const auto ro = buf_rsrc(o + in.t0 * Hv * 128, n * Hv * 128 * ES);
+    const auto pf = PR::reg16(f32x4{pv[0], pv[1], pv[2], pv[3]});
+    const float gt = Wl[64 + r16];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x4 pu = PR::mma16(PR::reg16(dl[b]), pf, zero4());
+      float ov[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = gt * qt[b][e] + pu[e];
+      PR::gstore4(ro, ((r16 * Hv + h) * 128 + v0 + 16 * b + 4 * kg) * ES, ov);
+    }
+  }
+
+  // S^T <- gamma_{n-1} S^T + K^T diag(d) D
+  if (advance) {
+    const float gl = __builtin_amdgcn_exp2f(Wl[n - 1]);
+    typename PR::F16 du[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = dl[b][e] * dec4[e];
+      du[b] = PR::reg16(t);
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      u[r] = row16_sum(u[r]);
-      if (WRITE_O) w[r] = row16_sum(w[r]);
-    }
+    for (int cb = 0; cb < 8; ++cb) {
+      const auto kt = PR::ldsT16(Ks, LDK, 16 * cb, lane);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float d = b * (vr[r] - a * u[r]);
+      for (int b = 0; b < 2; ++b) {
+        f32x4 acc;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) S.s[r][j] = __builtin_fmaf(d, kv[j], a * S.s[r][j]);
-      if (WRITE_O) {
-        const float orow = __builtin_fmaf(d, kq, a * w[r]);
-        if (cl == r) Act<T>::store1(o + ((int64_t)t * Hv + h) * 128 + rg + 16 * r, orow);
+        for (int e = 0; e < 4; ++e) acc[e] = gl * st[b][cb][e];
+        st[b][cb] = PR::mma16(kt, du[b], acc);
       }
     }
   }
 }
 
+// Runs tokens [bos, bos + len) of one (sequence, v-head) through this
+// wave's 32 state rows in st; `in` holds the first block's token inputs,
+// already requested by the caller (with the state), so a unit's loads are
+// in flight together.  WITH_O writes o; the state is advanced over every
+// block except, when !write_state, the last.
+template <class T, bool WITH_O>
+__device__ __forceinline__ void run_window(StepSmem<T>& sm, int wave, int lane, f32x4 (&st)[2][8],
+                                           BlockIn<T, WITH_O>& in, const T* q, const T* k,
+                                           const T* v, const float* g, const float* beta, T* o,
+                                           int bos, int len, int Hk, int Hv, int h, int kh,
+                                           bool write_state) {
+  const int v0 = 32 * wave;
+  run_block<T, WITH_O>(sm, wave, lane, st, in, o, Hv, h, write_state || len > kWin);
+  for (int c0 = kWin; c0 < len; c0 += kWin) {
+    load_block<T, WITH_O>(in, lane, q, k, v, g, beta, (int64_t)bos + c0, min(kWin, len - c0), Hk, Hv,
+                          h, kh, v0);
+    run_block<T, WITH_O>(sm, wave, lane, st, in, o, Hv, h, write_state || c0 + kWin < len);
+  }
+}
+
+__device__ __forceinline__ void zero_state(f32x4 (&st)[2][8]) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) st[b][cb] = zero4();
+}
+
+// One workgroup per (sequence, v-head).  The state is read unconditionally
+// right after the first block's token inputs (a state without an initial
+// value is read and then discarded), so no load waits on the flag.
 template <class T>
-__global__ __launch_bounds__(kStepThreads) void step_kernel(
+__global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 3 : 2) void step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int Hk, int Hv, float* state, const uint8_t* __restrict__ has_init, T* __restrict__ o,
     int commit_state) {
+  __shared__ StepSmem<T> sm;
   const int s = blockIdx.x / Hv;
   const int h = blockIdx.x % Hv;
   const int kh = h / (Hv / Hk);
-  const int rg = threadIdx.x >> 4, cl = threadIdx.x & 15;
-  const int bos = cu[s], eos = cu[s + 1];
-  if (eos <= bos) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int v0 = 32 * wave;
+  const int bos = cu[s], len = cu[s + 1] - bos;
+  if (len <= 0) return;
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
-  StateRegs S;
-  if (has_init == nullptr || has_init[s] != 0) {
-    load_state(base, rg, cl, S);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) S.s[r][j] = 0.f;
-  }
-  run_tokens<T, true>(S, q, k, v, g, beta, o, bos, eos, Hk, Hv, h, kh, rg, cl);
-  if (commit_state) store_state(base, rg, cl, S);
+  const bool init = has_init == nullptr || has_init[s] != 0;
+  BlockIn<T, true> in;
+  load_block<T, true>(in, lane, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
+  f32x4 st[2][8];
+  load_state(base, true, v0, r16, kg, st);
+  if (!init) zero_state(st);
+  run_window<T, true>(sm, wave, lane, st, in, q, k, v, g, beta, o, bos, len, Hk, Hv, h, kh,
+                      commit_state != 0);
+  if (commit_state) store_state(base, v0, r16, kg, st);
 }
 
 // One launch for all layers: block b covers (layer, sequence, role); roles
@@ -150,10 +343,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(
 // of one 2048-channel group.  A block whose sequence keeps no token exits
 // before touching memory.
 template <class T>
-__global__ __launch_bounds__(kStepThreads) void commit_kernel(
+__global__ __launch_bounds__(kStepThreads, 2) void commit_kernel(
     const gdn_layer_io* __restrict__ layers, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ n_keep, const uint8_t* __restrict__ has_init, int nseq, int C,
     int Hk, int Hv, int roles) {
+  __shared__ StepSmem<T> sm;
   const int b = blockIdx.x;
   const int role = b % roles;
   const int s = (b / roles) % nseq;
@@ -166,20 +360,19 @@ __global__ __launch_bounds__(kStepThreads) void commit_kernel(
   if (role < Hv) {
     const int h = role;
     const int kh = h / (Hv / Hk);
-    const int rg = threadIdx.x >> 4, cl = threadIdx.x & 15;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kg = lane >> 4;
     float* base = io.state + ((int64_t)s * Hv + h) * (128 * 128);
-    StateRegs S;
-    if (init) {
-      load_state(base, rg, cl, S);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) S.s[r][j] = 0.f;
-    }
-    run_tokens<T, false>(S, nullptr, static_cast<const T*>(io.k), static_cast<const T*>(io.v),
-                         io.g, io.beta, nullptr, bos, bos + n, Hk, Hv, h, kh, rg, cl);
-    store_state(base, rg, cl, S);
+    f32x4 st[2][8];
+    BlockIn<T, false> in;
+    load_block<T, false>(in, lane, nullptr, static_cast<const T*>(io.k), static_cast<const T*>(io.v), io.g,
+                         io.beta, bos, min(kWin, n), Hk, Hv, h, kh, 32 * wave);
+    load_state(base, init, 32 * wave, r16, kg, st);
+    run_window<T, false>(sm, wave, lane, st, in, nullptr, static_cast<const T*>(io.k),
+                         static_cast<const T*>(io.v), io.g, io.beta, nullptr, bos, n, Hk, Hv, h, kh,
+                         true);
+    store_state(base, 32 * wave, r16, kg, st);
   } else {
     const int c0 = ((role - Hv) * kStepThreads + threadIdx.x) * 8;
     if (c0 >= C) return;
@@ -226,7 +419,7 @@ hipError_t launch_step(const void* q, const void* k, const void* v, int act, con
                        const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
                        float* state, const uint8_t* has_init, void* o, int commit_state,
                        hipStream_t st) {
-  dim3 grid(nseq * Hv);
+  const dim3 grid(nseq * Hv);
   if (act == GDN_F32) {
     hipLaunchKernelGGL(step_kernel<float>, grid, dim3(kStepThreads), 0, st,
                        static_cast<const float*>(q), static_cast<const float*>(k),

@@ -302,10 +302,14 @@ def test_step_parity(act, commit):
         assert torch.equal(out["state"].cpu(), lb.state)
 
 
-def test_step_multi_token_equals_single_token_steps():
+def test_step_window_agrees_with_single_token_steps():
+    """T tokens in one call and T one-token calls evaluate the same
+    recurrence with a different association (a call's window runs its
+    products on MFMA over all of its tokens at once): equal within the
+    recurrence bound, token by token and for the final state."""
     geo = I.GEO_TINY
-    lengths = [1, 4, 8, 2]
-    lb, out = _step_run("bf16", geo, lengths, [1, 1, 1, 0], 500, True)
+    lengths = [1, 4, 8, 2, 16, 19]
+    lb, out = _step_run("bf16", geo, lengths, [1, 1, 1, 0, 1, 1], 500, True)
     cu = lb.cu_seqlens.tolist()
     for s in range(len(lengths)):
         st = lb.state[s:s + 1].to(DEV).contiguous()
@@ -318,8 +322,35 @@ def test_step_multi_token_equals_single_token_steps():
                                          out["v"][sl].contiguous(), out["g"][sl].contiguous(),
                                          out["beta"][sl].contiguous(), one, st, init,
                                          commit_state=True)
-            assert torch.equal(o1, out["o"][sl]), f"seq {s} token {t}"
-        assert torch.equal(st[0], out["state"][s]), f"seq {s} state"
+            TL.check_normwise(TL.np64(o1), TL.np64(out["o"][sl]), TL.REC_BF16, axes=(2,),
+                              what=f"seq {s} token {t}")
+        TL.check_normwise(TL.np64(st[0]), TL.np64(out["state"][s]), TL.REC_BF16, axes=(1, 2),
+                          what=f"seq {s} state")
+
+
+def test_step_single_token_window_matches_per_token_formula_f32():
+    """One-token windows in float32: o = a S q + d (k . q) with
+    d = b (v - a S k), the per-token update written out, to the float32
+    recurrence bound."""
+    geo = I.GEO_TINY
+    lengths = [1, 1, 1]
+    lb, out = _step_run("f32", geo, lengths, [1, 1, 1], 510, True)
+    torch.cuda.synchronize()
+    S = TL.np64(lb.state)
+    q, k, v = TL.np64(out["q"]), TL.np64(out["k"]), TL.np64(out["v"])
+    g, b = TL.np64(lb.g), TL.np64(lb.beta)
+    for s in range(3):
+        for h in range(geo.Hv):
+            kh = h // (geo.Hv // geo.Hk)
+            a = np.exp(g[s, h])
+            u = S[s, h] @ k[s, kh]
+            d = b[s, h] * (v[s, h] - a * u)
+            o_ref = a * (S[s, h] @ q[s, kh]) + d * (k[s, kh] @ q[s, kh])
+            st_ref = a * S[s, h] + np.outer(d, k[s, kh])
+            TL.check_normwise(TL.np64(out["o"][s, h])[None], o_ref[None], TL.REC_F32, axes=(1,),
+                              what="o")
+            TL.check_normwise(TL.np64(out["state"][s, h])[None], st_ref[None], TL.REC_F32,
+                              axes=(1, 2), what="state")
 
 
 def test_prefill_and_step_agree_within_tolerance():
