@@ -6,11 +6,16 @@
 // tokens):  y[t][c] = bias[c] + sum_j w[c][j] * xe[t-3+j][c], where xe is the
 // sequence input preceded by its 3 stored rows (oldest first).
 //
-// Layout: one workgroup per (chunk, group of 512 channels); each lane owns
-// 8 adjacent channels, so every token row is read and written with 16-byte
-// accesses; each of the 4 waves takes 16 of the chunk's tokens and walks them
-// in order keeping the 3-token window in registers (no cross-lane traffic,
-// no LDS).  A wave reads its 3-row halo from x unless it starts a sequence.
+// Layout: one workgroup per (chunk, group of 256 channels); each lane owns
+// 4 adjacent channels, so a wave reads and writes every token row as one
+// contiguous 512-byte (bf16) span; each of the 4 waves takes 16 of the
+// chunk's tokens, requests all of its rows up front and walks them in order
+// with the 3-token window in registers (no cross-lane traffic, no LDS).  A
+// wave reads its 3-row halo from x unless it starts a sequence.  Outputs
+// are written through a buffer resource spanning exactly the wave's tokens,
+// so rows past a chunk's end need no branches.  Four channels per lane keep
+// the kernel near 100 registers, so five workgroups share a CU and the
+// loads of some overlap the stores of others.
 //
 // conv_state ownership: only wave 0 of the FIRST chunk's workgroup touches a
 // sequence's conv_state.  Its lanes read the stored rows, use them for the
@@ -21,16 +26,16 @@
 // conv_state in place cannot race with any other workgroup.  This replaces
 // the "last chunk writes" arrangement whose cross-block race the issue
 // describes.
-#include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma.hpp"
 
 namespace gdn {
 
 namespace {
 
 constexpr int kConvThreads = 256;                 // 4 waves
-constexpr int kConvChannelsPerLane = 8;
-constexpr int kConvChannelsPerBlock = 64 * kConvChannelsPerLane;   // 512
+constexpr int kConvChannelsPerLane = 4;
+constexpr int kConvChannelsPerBlock = 64 * kConvChannelsPerLane;   // 256
 constexpr int kConvTokensPerWave = 16;            // 4 waves x 16 = one 64-token chunk
 
 // ------------------------------------------------------------ chunk builder
@@ -95,100 +100,103 @@ __global__ __launch_bounds__(256) void make_chunks_kernel(const int32_t* __restr
 // independent 16-byte loads), then computes and stores 16 outputs.  Only
 // wave 0 of a sequence's first chunk touches conv_state (see the file
 // comment).
+// Four adjacent activations in storage form.
+template <class T> struct Act4;
+template <> struct Act4<float> {
+  using Raw = float4;
+  __device__ __forceinline__ static Raw load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ static void unpack(Raw r, float (&v)[4]) { v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w; }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t rs, int off, const float (&v)[4]) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                                 __float_as_uint(v[3])}, rs, off, 0, 0);
+  }
+};
+template <> struct Act4<uint16_t> {
+  using Raw = uint2;
+  __device__ __forceinline__ static Raw load(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ static void unpack(Raw r, float (&v)[4]) {
+    v[0] = bf16_to_f32(r.x & 0xffffu); v[1] = bf16_to_f32(r.x >> 16);
+    v[2] = bf16_to_f32(r.y & 0xffffu); v[3] = bf16_to_f32(r.y >> 16);
+  }
+  __device__ __forceinline__ static void store(__amdgpu_buffer_rsrc_t rs, int off, const float (&v)[4]) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs, off, 0, 0);
+  }
+};
+
 template <class T>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
     float* conv_state, const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu,
     const gdn_chunk* __restrict__ chunks, int C, int write_state, T* __restrict__ y) {
+  using A = Act4<T>;
   const gdn_chunk ch = chunks[blockIdx.x];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c0 = (blockIdx.y * 64 + lane) * kConvChannelsPerLane;
   if (ch.seq < 0 || c0 >= C) return;
   const int s = ch.seq;
   const int t_begin = ch.begin + kConvTokensPerWave * wave;
-  const int t_end = min(t_begin + kConvTokensPerWave, ch.end);
+  const int n = min(kConvTokensPerWave, ch.end - t_begin);
   const bool owner = wave == 0 && (ch.flags & GDN_CHUNK_FIRST) != 0;   // reads and writes conv_state
-  if (t_begin >= t_end && !owner) return;
+  if (n <= 0) return;   // an owner's range is never empty: a first chunk starts its sequence
+
+  // all token rows of this wave, requested before any use (rows past the
+  // chunk's end re-read its last row; their outputs are dropped)
+  typename A::Raw xr[kConvTokensPerWave];
+#pragma unroll
+  for (int u = 0; u < kConvTokensPerWave; ++u)
+    xr[u] = A::load(x + (int64_t)(t_begin + min(u, n - 1)) * xs + c0);
 
   // window rows xe[t-3], xe[t-2], xe[t-1] for t = t_begin
-  float h0[8], h1[8], h2[8];
+  float h0[4], h1[4], h2[4];
   float* st = conv_state + ((int64_t)s * 3) * C + c0;
-  const bool init = has_init == nullptr || has_init[s] != 0;
   if (owner) {
-    if (init) {
-#pragma unroll
-      for (int i = 0; i < 8; i += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(st + i);
-        const float4 bb = *reinterpret_cast<const float4*>(st + C + i);
-        const float4 c = *reinterpret_cast<const float4*>(st + 2 * C + i);
-        h0[i] = a.x; h0[i + 1] = a.y; h0[i + 2] = a.z; h0[i + 3] = a.w;
-        h1[i] = bb.x; h1[i + 1] = bb.y; h1[i + 2] = bb.z; h1[i + 3] = bb.w;
-        h2[i] = c.x; h2[i + 1] = c.y; h2[i + 2] = c.z; h2[i + 3] = c.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { h0[i] = 0.f; h1[i] = 0.f; h2[i] = 0.f; }
-    }
+    const bool init = has_init == nullptr || has_init[s] != 0;
+    const float4 a = init ? *reinterpret_cast<const float4*>(st) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 bb = init ? *reinterpret_cast<const float4*>(st + C) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 c = init ? *reinterpret_cast<const float4*>(st + 2 * C) : make_float4(0.f, 0.f, 0.f, 0.f);
+    h0[0] = a.x; h0[1] = a.y; h0[2] = a.z; h0[3] = a.w;
+    h1[0] = bb.x; h1[1] = bb.y; h1[2] = bb.z; h1[3] = bb.w;
+    h2[0] = c.x; h2[1] = c.y; h2[2] = c.z; h2[3] = c.w;
   } else {
     // the 3 rows before t_begin lie in the same sequence: a non-first chunk
     // starts at least 64 tokens in, and waves > 0 start 16 w tokens in
-    Act<T>::load8(x + (int64_t)(t_begin - 3) * xs + c0, h0);
-    Act<T>::load8(x + (int64_t)(t_begin - 2) * xs + c0, h1);
-    Act<T>::load8(x + (int64_t)(t_begin - 1) * xs + c0, h2);
+    A::unpack(A::load(x + (int64_t)(t_begin - 3) * xs + c0), h0);
+    A::unpack(A::load(x + (int64_t)(t_begin - 2) * xs + c0), h1);
+    A::unpack(A::load(x + (int64_t)(t_begin - 1) * xs + c0), h2);
   }
   // the stored rows, kept for sequences shorter than 3 tokens
-  float i0[8], i1[8], i2[8];
+  float o1[4], o2[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { i0[i] = h0[i]; i1[i] = h1[i]; i2[i] = h2[i]; }
+  for (int i = 0; i < 4; ++i) { o1[i] = h1[i]; o2[i] = h2[i]; }
 
-  float w0[8], w1[8], w2[8], w3[8], b[8];
+  float w0[4], w1[4], w2[4], w3[4], b[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const float4 wv = *reinterpret_cast<const float4*>(w + (int64_t)(c0 + i) * 4);
     w0[i] = wv.x; w1[i] = wv.y; w2[i] = wv.z; w3[i] = wv.w;
     b[i] = 0.f;
   }
   if (bias != nullptr) {
-    const float4 b0 = *reinterpret_cast<const float4*>(bias + c0);
-    const float4 b1 = *reinterpret_cast<const float4*>(bias + c0 + 4);
-    b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w;
-    b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+    const float4 bv = *reinterpret_cast<const float4*>(bias + c0);
+    b[0] = bv.x; b[1] = bv.y; b[2] = bv.z; b[3] = bv.w;
   }
 
-  // all token rows of this wave, loaded before any use (rows past t_end
-  // re-read row t_begin and are never stored)
-  typename Act<T>::Raw xr[kConvTokensPerWave];
+  const auto ry = buf_rsrc(y + (int64_t)t_begin * C, n * C * (int)sizeof(T));
 #pragma unroll
   for (int u = 0; u < kConvTokensPerWave; ++u) {
-    const int t = (t_begin + u < t_end) ? t_begin + u : t_begin;
-    xr[u] = Act<T>::load_raw(x + (int64_t)t * xs + c0);
-  }
-  float x0[8], x1[8];   // the first two rows, kept for sequences shorter than 3 tokens
+    float xv[4], out[4];
+    A::unpack(xr[u], xv);
 #pragma unroll
-  for (int u = 0; u < kConvTokensPerWave; ++u) {
-    if (t_begin + u < t_end) {
-      float xv[8], out[8];
-      Act<T>::unpack(xr[u], xv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float acc = b[i];
-        acc = __builtin_fmaf(w0[i], h0[i], acc);
-        acc = __builtin_fmaf(w1[i], h1[i], acc);
-        acc = __builtin_fmaf(w2[i], h2[i], acc);
-        acc = __builtin_fmaf(w3[i], xv[i], acc);
-        out[i] = acc;
-        h0[i] = h1[i]; h1[i] = h2[i]; h2[i] = xv[i];
-      }
-      if (u == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x0[i] = xv[i];
-      }
-      if (u == 1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x1[i] = xv[i];
-      }
-      Act<T>::store8(y + (int64_t)(t_begin + u) * C + c0, out);
+    for (int i = 0; i < 4; ++i) {
+      float acc = b[i];
+      acc = __builtin_fmaf(w0[i], h0[i], acc);
+      acc = __builtin_fmaf(w1[i], h1[i], acc);
+      acc = __builtin_fmaf(w2[i], h2[i], acc);
+      acc = __builtin_fmaf(w3[i], xv[i], acc);
+      out[i] = acc;
+      h0[i] = h1[i]; h1[i] = h2[i]; h2[i] = xv[i];
     }
+    A::store(ry, (u * C + c0) * (int)sizeof(T), out);
   }
 
   if (owner && write_state) {
@@ -196,24 +204,23 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     const int len = eos - bos;
     // final rows r = 0..2 are xe[len-3+r]: x when that index is >= 0, else the
     // stored row 3 + (len-3+r).
-    float r0[8], r1[8], r2[8];
+    float r0[4], r1[4], r2[4], x0[4], x1[4];
+    A::unpack(xr[0], x0);
+    A::unpack(xr[1], x1);
     if (len >= 3) {
-      Act<T>::load8(x + (int64_t)(eos - 3) * xs + c0, r0);
-      Act<T>::load8(x + (int64_t)(eos - 2) * xs + c0, r1);
-      Act<T>::load8(x + (int64_t)(eos - 1) * xs + c0, r2);
+      A::unpack(A::load(x + (int64_t)(eos - 3) * xs + c0), r0);
+      A::unpack(A::load(x + (int64_t)(eos - 2) * xs + c0), r1);
+      A::unpack(A::load(x + (int64_t)(eos - 1) * xs + c0), r2);
     } else if (len == 2) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { r0[i] = i2[i]; r1[i] = x0[i]; r2[i] = x1[i]; }
+      for (int i = 0; i < 4; ++i) { r0[i] = o2[i]; r1[i] = x0[i]; r2[i] = x1[i]; }
     } else {  // len == 1 (a first chunk is never empty)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { r0[i] = i1[i]; r1[i] = i2[i]; r2[i] = x0[i]; }
+      for (int i = 0; i < 4; ++i) { r0[i] = o1[i]; r1[i] = o2[i]; r2[i] = x0[i]; }
     }
-#pragma unroll
-    for (int i = 0; i < 8; i += 4) {
-      *reinterpret_cast<float4*>(st + i) = make_float4(r0[i], r0[i + 1], r0[i + 2], r0[i + 3]);
-      *reinterpret_cast<float4*>(st + C + i) = make_float4(r1[i], r1[i + 1], r1[i + 2], r1[i + 3]);
-      *reinterpret_cast<float4*>(st + 2 * C + i) = make_float4(r2[i], r2[i + 1], r2[i + 2], r2[i + 3]);
-    }
+    *reinterpret_cast<float4*>(st) = make_float4(r0[0], r0[1], r0[2], r0[3]);
+    *reinterpret_cast<float4*>(st + C) = make_float4(r1[0], r1[1], r1[2], r1[3]);
+    *reinterpret_cast<float4*>(st + 2 * C) = make_float4(r2[0], r2[1], r2[2], r2[3]);
   }
 }
 
