@@ -8,6 +8,8 @@
  *   4. chunked gated delta-rule prefill          gdn_delta_rule_prefill
  *   5. per-token decode / verify step            gdn_delta_rule_step
  *   6. layer-batched commit of a verify window   gdn_commit
+ *   7. fused decode / verify: conv + post-conv + step in one launch
+ *                                                gdn_decode_fused
  *
  * Sources (page title, section):
  *   "perf(gdn): optimize post-conv and causal-conv kernels" (vllm.cpp pull
@@ -220,6 +222,29 @@ int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act,
 int gdn_commit(const gdn_layer_io* layers, int L, const int32_t* cu_seqlens,
                const int32_t* n_keep, const uint8_t* has_initial_state, int nseq,
                int C, int Hk, int Hv, int dk, int dv, int act, void* stream);
+
+/* ---- 7. fused decode / verify step ------------------------------------------
+ * One launch per layer for decode tokens and draft windows: the causal conv
+ * of each sequence's tokens (stored conv rows as history), SiLU, the q / k
+ * L2 norm and the recurrence step, without writing y, q, k or v to memory.
+ * The result is bitwise equal to gdn_causal_conv_fwd (write_state =
+ * write_conv_state) + gdn_postconv_l2 (out dtype = act) +
+ * gdn_delta_rule_step (commit_state) on the same inputs.  One workgroup per
+ * (sequence, k-head) owns the k-head's q, k channels and the v channels of
+ * its v-heads, so the in-place conv_state update is race-free.
+ * Fuses the three calls that "Summary" items 2-3 ("Strata pull request
+ * 3226") keep as separate verify-forward launches.
+ *   x, x_row_stride, w, bias, conv_state: as gdn_causal_conv_fwd
+ *   g, beta, state, has_initial_state, o: as gdn_delta_rule_step
+ *   Hv must equal Hk or 2*Hk (GDN_ERR_SHAPE otherwise); eps > 0.
+ *   o, state and conv_state must not overlap x or each other. */
+int gdn_decode_fused(const void* x, int64_t x_row_stride, int act,
+                     const float* w, const float* bias, float* conv_state,
+                     const int32_t* cu_seqlens, int nseq, int N,
+                     int Hk, int Hv, int dk, int dv, float eps,
+                     const float* g, const float* beta, float* state,
+                     const uint8_t* has_initial_state, void* o,
+                     int write_conv_state, int commit_state, void* stream);
 
 #ifdef __cplusplus
 }

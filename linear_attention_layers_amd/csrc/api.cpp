@@ -199,6 +199,37 @@ int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act, co
                   "delta_rule_step");
 }
 
+int gdn_decode_fused(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                     float* conv_state, const int32_t* cu, int nseq, int N, int Hk, int Hv, int dk,
+                     int dv, float eps, const float* g, const float* beta, float* state,
+                     const uint8_t* has_init, void* o, int write_conv_state, int commit_state,
+                     void* stream) {
+  if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
+  if (nseq < 0 || N < 0) return fail(GDN_ERR_SHAPE, "negative nseq or N");
+  int st = check_heads(Hk, Hv, dk, dv);
+  if (st != GDN_OK) return st;
+  if (Hv != Hk && Hv != 2 * Hk) return fail(GDN_ERR_SHAPE, "the fused step needs Hv = Hk or Hv = 2*Hk (got Hk=%d Hv=%d)", Hk, Hv);
+  if (!(eps > 0.f)) return fail(GDN_ERR_SHAPE, "eps must be > 0");
+  const int C = 2 * Hk * dk + Hv * dv;
+  if (xs < C) return fail(GDN_ERR_SHAPE, "x_row_stride must be >= C");
+  if (nseq == 0 || N == 0) return GDN_OK;
+  if (!x || !w || !conv_state || !cu || !g || !beta || !state || !o)
+    return fail(GDN_ERR_NULL, "x, w, conv_state, cu_seqlens, g, beta, state and o are required");
+  const size_t e = elem_bytes(act);
+  if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || (bias && !aligned16(bias)) ||
+      !aligned16(conv_state) || !aligned16(state) || !aligned16(o))
+    return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state, state and o must be 16-byte aligned");
+  const size_t nx = ((size_t)(N - 1) * xs + C) * e, ncs = (size_t)nseq * 3 * C * 4;
+  const size_t no = (size_t)N * Hv * dv * e, ns = (size_t)nseq * Hv * dv * dk * 4;
+  if (overlaps(o, no, x, nx) || overlaps(o, no, conv_state, ncs) || overlaps(o, no, state, ns) ||
+      overlaps(state, ns, x, nx) || overlaps(state, ns, conv_state, ncs) || overlaps(conv_state, ncs, x, nx))
+    return fail(GDN_ERR_ALIAS, "o, state and conv_state must not overlap x or each other");
+  return launched(gdn::launch_decode_fused(x, xs, act, w, bias, conv_state, cu, nseq, Hk, Hv, eps, g, beta,
+                                           state, has_init, o, write_conv_state, commit_state,
+                                           as_stream(stream)),
+                  "decode_fused");
+}
+
 int gdn_commit(const gdn_layer_io* layers, int L, const int32_t* cu, const int32_t* n_keep,
                const uint8_t* has_init, int nseq, int C, int Hk, int Hv, int dk, int dv, int act,
                void* stream) {

@@ -117,4 +117,48 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------- post-conv math
+// Shared by the post-conv kernel and the fused decode kernel, so both give
+// bit-identical q, k, v.  A head's 128 channels sit in one 16-lane DPP row,
+// 8 adjacent channels per lane.
+// SiLU for a float32 output is evaluated in float64 and rounded once, so the
+// float32 output arm carries the correctly rounded activation; for a bf16
+// output float32 arithmetic suffices (its error is far below a bf16 step).
+template <class TO> __device__ __forceinline__ float silu(float y);
+template <> __device__ __forceinline__ float silu<float>(float y) {
+  const double d = static_cast<double>(y);
+  return static_cast<float>(d / (1.0 + exp(-d)));
+}
+template <> __device__ __forceinline__ float silu<uint16_t>(float y) {
+  // y * 1 / (1 + 2^(-y log2 e)) with the hardware exp2 and reciprocal (each
+  // about 1 ulp): a few float32 ulps in all, far below a bf16 step.
+  // Large |y| saturates correctly: 2^(+inf) = inf -> rcp = 0 -> -0.
+  const float e = __builtin_amdgcn_exp2f(-y * 1.4426950408889634f);
+  return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float head_sum_sq(const float (&s)[8]) {
+#pragma clang fp contract(off)
+  const float p0 = s[0] * s[0] + s[1] * s[1];
+  const float p1 = s[2] * s[2] + s[3] * s[3];
+  const float p2 = s[4] * s[4] + s[5] * s[5];
+  const float p3 = s[6] * s[6] + s[7] * s[7];
+  const float lane = (p0 + p1) + (p2 + p3);
+  return row16_sum(lane);
+}
+
+
+// q_hat (is_qk) or v of one lane's 8 channels from its 8 conv outputs
+// (already in the activation dtype); every lane of the row must call it.
+template <class TO>
+__device__ __forceinline__ void postconv_lane(const float (&raw)[8], bool is_qk, float eps, float (&out)[8]) {
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = silu<TO>(raw[i]);
+  const float sum = head_sum_sq(s);
+  const float inv = 1.0f / __builtin_sqrtf(sum + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = is_qk ? s[i] * inv : s[i];
+}
+
 }  // namespace gdn

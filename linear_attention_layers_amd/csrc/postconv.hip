@@ -27,32 +27,6 @@ constexpr int kPostThreads = 256;
 constexpr int kPostChannelsPerBlock = kPostThreads * 8;
 constexpr int kPostTokensPerBlock = 4;
 
-// SiLU for a float32 output is evaluated in float64 and rounded once, so the
-// float32 output arm carries the correctly rounded activation; for a bf16
-// output float32 arithmetic suffices (its error is far below a bf16 step).
-template <class TO> __device__ __forceinline__ float silu(float y);
-template <> __device__ __forceinline__ float silu<float>(float y) {
-  const double d = static_cast<double>(y);
-  return static_cast<float>(d / (1.0 + exp(-d)));
-}
-template <> __device__ __forceinline__ float silu<uint16_t>(float y) {
-  // y * 1 / (1 + 2^(-y log2 e)) with the hardware exp2 and reciprocal (each
-  // about 1 ulp): a few float32 ulps in all, far below a bf16 step.
-  // Large |y| saturates correctly: 2^(+inf) = inf -> rcp = 0 -> -0.
-  const float e = __builtin_amdgcn_exp2f(-y * 1.4426950408889634f);
-  return y * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-__device__ __forceinline__ float head_sum_sq(const float (&s)[8]) {
-#pragma clang fp contract(off)
-  const float p0 = s[0] * s[0] + s[1] * s[1];
-  const float p1 = s[2] * s[2] + s[3] * s[3];
-  const float p2 = s[4] * s[4] + s[5] * s[5];
-  const float p3 = s[6] * s[6] + s[7] * s[7];
-  const float lane = (p0 + p1) + (p2 + p3);
-  return row16_sum(lane);
-}
-
 template <class TI, class TO>
 __global__ __launch_bounds__(kPostThreads) void postconv_kernel(
     const TI* __restrict__ y, int64_t ys, int N, int C, int Hk, int Hv, float eps,

@@ -338,6 +338,175 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 3 : 2) void step_ker
   if (commit_state) store_state(base, v0, r16, kg, st);
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode / verify step: the causal conv over the window's x rows, SiLU,
+// the q / k L2 norm and the step in one launch, with y, q, k and v kept on
+// chip.  One workgroup per (sequence, k-head) holds the G = Hv / Hk v-heads
+// that read that k-head (4 waves each), so it owns every channel it reads:
+// q and k of the k-head and v of its v-heads.  Its optional in-place
+// conv_state update therefore cannot race with another workgroup.
+//
+// Per block of up to 16 tokens: phase A computes y, rounds it to the
+// activation dtype (as the stored y would be), applies the post-conv lane
+// function (as the post-conv kernel does) and writes q, k and each v-head's
+// v, rounded again, into LDS tiles; phase B runs the step's block function
+// on fragments read from those tiles.  Every value is what the three
+// separate launches produce, so the results are bitwise equal to them.
+template <class T, int G> struct FusedSmem {
+  using E = typename Prec<T>::E;
+  static constexpr int LDK = 128 + Prec<T>::PAD;
+  StepSmem<T> step[G];
+  E Qs[kWin * LDK];
+  E Ks[kWin * LDK];
+  E Vs[G][kWin * LDK];
+};
+
+template <class T, int G>
+__global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
+    const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
+    float* conv_state, const int32_t* __restrict__ cu, int Hk, int Hv, float eps,
+    const float* __restrict__ g, const float* __restrict__ beta, float* state,
+    const uint8_t* __restrict__ has_init, T* __restrict__ o, int write_conv_state, int commit_state) {
+  using PR = Prec<T>;
+  using E = typename PR::E;
+  constexpr int LDK = FusedSmem<T, G>::LDK;
+  __shared__ FusedSmem<T, G> sm;
+  const int s = blockIdx.x / Hk, kh = blockIdx.x % Hk;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wl = wave & 3;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int v0 = 32 * wl;
+  const int h = kh * G + grp;
+  const int C = (2 * Hk + Hv) * 128;
+  const int bos = cu[s], len = cu[s + 1] - bos;
+  if (len <= 0) return;
+  const bool init = has_init == nullptr || has_init[s] != 0;
+  float* cs = conv_state + (int64_t)s * 3 * C;
+
+  f32x4 st[2][8];
+  float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
+  load_state(base, true, v0, r16, kg, st);
+  if (!init) zero_state(st);
+
+  // phase A unit = (token, head) on one 16-lane row; head 0 = q, 1 = k,
+  // 2 + j = v of v-head kh * G + j; lane j of the row owns channels 8j..8j+7
+  const int row = tid >> 4, jl = tid & 15;
+  auto channel = [&](int hd) {
+    return (hd == 0 ? kh * 128 : hd == 1 ? (Hk + kh) * 128 : (2 * Hk + kh * G + hd - 2) * 128) + 8 * jl;
+  };
+  for (int c0 = 0; c0 < len; c0 += kWin) {
+    const int n = min(kWin, len - c0);
+    for (int unit = row; unit < kWin * (2 + G); unit += 16 * G) {
+      const int tok = unit % kWin, hd = unit / kWin;
+      const int ch = channel(hd);
+      float out[8];
+      if (tok < n) {
+        const int t = c0 + tok;   // window-relative token
+        float xe[4][8];           // xe[t-3 .. t]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = t - 3 + r;
+          if (tr >= 0) {
+            Act<T>::load8(x + (int64_t)(bos + tr) * xs + ch, xe[r]);
+          } else if (init) {
+            const float* p = cs + (int64_t)(3 + tr) * C + ch;
+            const float4 a = *reinterpret_cast<const float4*>(p), b4 = *reinterpret_cast<const float4*>(p + 4);
+            xe[r][0] = a.x; xe[r][1] = a.y; xe[r][2] = a.z; xe[r][3] = a.w;
+            xe[r][4] = b4.x; xe[r][5] = b4.y; xe[r][6] = b4.z; xe[r][7] = b4.w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xe[r][i] = 0.f;
+          }
+        }
+        float yv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 wv = *reinterpret_cast<const float4*>(w + (int64_t)(ch + i) * 4);
+          float acc = bias != nullptr ? bias[ch + i] : 0.f;
+          acc = __builtin_fmaf(wv.x, xe[0][i], acc);
+          acc = __builtin_fmaf(wv.y, xe[1][i], acc);
+          acc = __builtin_fmaf(wv.z, xe[2][i], acc);
+          acc = __builtin_fmaf(wv.w, xe[3][i], acc);
+          yv[i] = acc;
+        }
+        // y as stored in the activation dtype
+        typename Act<T>::Raw ry;
+        {
+          E tmp[8];
+          Act<T>::store8(tmp, yv);
+          ry = Act<T>::load_raw(tmp);
+        }
+        Act<T>::unpack(ry, yv);
+        postconv_lane<T>(yv, hd < 2, eps, out);
+      } else {
+        // every lane of the row takes part in the row reduction
+        float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        postconv_lane<T>(zero, false, eps, out);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = 0.f;
+      }
+      E* dst = hd == 0 ? sm.Qs : hd == 1 ? sm.Ks : sm.Vs[hd - 2];
+      Act<T>::store8(dst + tok * LDK + 8 * jl, out);
+    }
+    __syncthreads();
+
+    // phase B: the step's block on this v-head group's 4 waves
+    BlockIn<T, true> in;
+    in.n = n;
+    in.t0 = (int64_t)bos + c0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      in.kf[t] = PR::lds32(sm.Ks, LDK, r16, 32 * t, kg);
+      in.qf[t] = PR::lds32(sm.Qs, LDK, r16, 32 * t, kg);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) in.vv[b][e] = PR::to_f32(sm.Vs[grp][(4 * kg + e) * LDK + v0 + 16 * b + r16]);
+    {
+      const auto rg = buf_rsrc(g + in.t0 * Hv, n * Hv * 4);
+      const auto rb = buf_rsrc(beta + in.t0 * Hv, n * Hv * 4);
+      const int goff = ((lane & 15) * Hv + h) * 4;
+      in.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
+      in.bl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, goff, 0, 0));
+    }
+    run_block<T, true>(sm.step[grp], wl, lane, st, in, o, Hv, h, commit_state != 0 || c0 + kWin < len);
+    __syncthreads();
+  }
+  if (commit_state) store_state(base, v0, r16, kg, st);
+
+  // conv_state <- the last 3 rows of [stored rows ; x window] for this
+  // workgroup's channels.  One 16-lane row per head reads all three final
+  // rows before writing any, so a row shifted down from a stored row is
+  // read and written by the same lane, in program order.
+  if (write_conv_state && row < 2 + G) {
+    const int ch = channel(row);
+    float v8[3][8];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int tr = len - 3 + r;   // xe index of final row r
+      if (tr >= 0) {
+        Act<T>::load8(x + (int64_t)(bos + tr) * xs + ch, v8[r]);
+      } else if (init) {
+        const float* p = cs + (int64_t)(3 + tr) * C + ch;
+        const float4 a = *reinterpret_cast<const float4*>(p), b4 = *reinterpret_cast<const float4*>(p + 4);
+        v8[r][0] = a.x; v8[r][1] = a.y; v8[r][2] = a.z; v8[r][3] = a.w;
+        v8[r][4] = b4.x; v8[r][5] = b4.y; v8[r][6] = b4.z; v8[r][7] = b4.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v8[r][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      float* p = cs + (int64_t)r * C + ch;
+      *reinterpret_cast<float4*>(p) = make_float4(v8[r][0], v8[r][1], v8[r][2], v8[r][3]);
+      *reinterpret_cast<float4*>(p + 4) = make_float4(v8[r][4], v8[r][5], v8[r][6], v8[r][7]);
+    }
+  }
+}
+
 // One launch for all layers: block b covers (layer, sequence, role); roles
 // 0..Hv-1 replay the state of v-head `role`, roles Hv.. shift the conv rows
 // of one 2048-channel group.  A block whose sequence keeps no token exits
@@ -431,6 +600,27 @@ hipError_t launch_step(const void* q, const void* k, const void* v, int act, con
                        static_cast<const uint16_t*>(v), g, beta, cu, Hk, Hv, state, has_init,
                        static_cast<uint16_t*>(o), commit_state);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fused(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                               float* conv_state, const int32_t* cu, int nseq, int Hk, int Hv, float eps,
+                               const float* g, const float* beta, float* state, const uint8_t* has_init,
+                               void* o, int write_conv_state, int commit_state, hipStream_t st) {
+  const int G = Hv / Hk;
+  const dim3 grid(nseq * Hk);
+#define GDN_FUSED_LAUNCH(TT, GG)                                                                   \
+  hipLaunchKernelGGL((fused_kernel<TT, GG>), grid, dim3(256 * GG), 0, st, static_cast<const TT*>(x), xs, w, \
+                     bias, conv_state, cu, Hk, Hv, eps, g, beta, state, has_init, static_cast<TT*>(o),     \
+                     write_conv_state, commit_state)
+  if (act == GDN_F32) {
+    if (G == 1) GDN_FUSED_LAUNCH(float, 1);
+    else GDN_FUSED_LAUNCH(float, 2);
+  } else {
+    if (G == 1) GDN_FUSED_LAUNCH(uint16_t, 1);
+    else GDN_FUSED_LAUNCH(uint16_t, 2);
+  }
+#undef GDN_FUSED_LAUNCH
   return hipGetLastError();
 }
 

@@ -81,10 +81,13 @@ _step = _sig("gdn_delta_rule_step", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _
                                      _i32, _i32, _vp, _vp, _vp, _i32, _vp])
 _commit = _sig("gdn_commit", [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                               _vp])
+_decode_fused = _sig("gdn_decode_fused", [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp])
 
 EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
             "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd",
-            "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_delta_rule_step", "gdn_commit"]
+            "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_delta_rule_step", "gdn_commit",
+            "gdn_decode_fused"]
 
 
 class GdnError(RuntimeError):
@@ -259,6 +262,30 @@ def gdn_delta_rule_step(q, k, v, g, beta, cu_seqlens, state, has_initial_state=N
     _check(_step(_ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                  nseq, N, Hk, Hv, dk, dv, _ptr(state), _ptr(has_initial_state), _ptr(o),
                  int(bool(commit_state)), _stream(stream)), "gdn_delta_rule_step")
+    return o
+
+
+def gdn_decode_fused(x, w, bias, conv_state, cu_seqlens, g, beta, state, Hk: int, Hv: int,
+                     eps: float = 1e-6, has_initial_state=None, o: Optional[torch.Tensor] = None,
+                     write_conv_state: bool = True, commit_state: bool = True,
+                     stream=None) -> torch.Tensor:
+    """conv + post-conv + step in one launch (bitwise equal to the three calls)."""
+    N, C = x.shape
+    _require(x.stride(1) == 1, "x rows must be contiguous")
+    for t, nm in ((w, "w"), (conv_state, "conv_state"), (g, "g"), (beta, "beta"), (state, "state")):
+        _dense(t, nm)
+    _require(w.dtype == torch.float32 and conv_state.dtype == torch.float32 and g.dtype == torch.float32
+             and beta.dtype == torch.float32 and state.dtype == torch.float32,
+             "w, conv_state, g, beta, state: float32")
+    _require(bias is None or bias.dtype == torch.float32, "bias: float32")
+    if o is None:
+        o = torch.empty(N, Hv, 128, dtype=x.dtype, device=x.device)
+    _dense(o, "o")
+    nseq = cu_seqlens.numel() - 1
+    _check(_decode_fused(_ptr(x), x.stride(0), _code(x.dtype), _ptr(w), _ptr(bias), _ptr(conv_state),
+                         _ptr(cu_seqlens), nseq, N, Hk, Hv, 128, 128, float(eps), _ptr(g), _ptr(beta),
+                         _ptr(state), _ptr(has_initial_state), _ptr(o), int(bool(write_conv_state)),
+                         int(bool(commit_state)), _stream(stream)), "gdn_decode_fused")
     return o
 
 

@@ -414,3 +414,68 @@ def test_commit_parity_and_bitwise_equal_to_step_commit():
                                 gdn.gdn_make_chunks_device(cu_keep, int(sum(n_keep))), True)
         assert torch.equal(st2, out["state"]), f"layer {layer}"
         assert torch.equal(cs2, out["conv_state"]), f"layer {layer}"
+
+
+# ---------------------------------------------------------------- fused decode
+
+FUSED_CASES = [
+    # act, geometry, lengths, has_init, write_conv_state, commit_state, bias_std
+    ("bf16", I.Geometry(Hk=2, Hv=4), [1, 3, 8, 0, 5, 2], [1, 1, 0, 1, 1, 0], True, True, 0.0),
+    ("bf16", I.Geometry(Hk=2, Hv=4), [1, 3, 8, 0, 5, 2], [1, 1, 0, 1, 1, 0], False, False, 0.3),
+    ("bf16", I.Geometry(Hk=2, Hv=2), [1, 1, 1, 2], [1, 1, 1, 1], True, True, 0.0),
+    ("bf16", I.Geometry(Hk=1, Hv=2), [17, 33, 4], [1, 0, 1], True, False, 0.0),
+    ("bf16", I.GEO_8192, [1, 1, 4, 1], [1, 1, 1, 0], True, True, 0.0),
+    ("f32", I.Geometry(Hk=2, Hv=4), [1, 7, 2, 16], [1, 0, 1, 1], True, True, 0.2),
+    ("f32", I.Geometry(Hk=2, Hv=2), [3, 1], [0, 1], False, True, 0.0),
+    ("f32", I.Geometry(Hk=1, Hv=1), [20, 0, 1], [1, 1, 0], True, True, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+def test_decode_fused_bitwise_equal_to_three_calls(case):
+    act, geo, lengths, hinit, wcs, commit, bias_std = FUSED_CASES[case]
+    lb = I.make_layer(geo, lengths, act, 800 + case, state_std=0.3, has_init=hinit,
+                      bias_std=bias_std)
+    cu = lb.cu_seqlens.to(DEV)
+    hi = lb.has_init.to(DEV)
+    x, w, b = lb.x.to(DEV), lb.conv_w.to(DEV), TL.dev(lb.conv_b)
+    g, beta = lb.g.to(DEV), lb.beta.to(DEV)
+    # the three calls
+    cs1, st1 = lb.conv_state.to(DEV), lb.state.to(DEV)
+    y = gdn.gdn_causal_conv_fwd(x, w, b, cs1, hi, cu, gdn.gdn_make_chunks_device(cu, lb.N), wcs)
+    q, k, v = gdn.gdn_postconv_l2(y, geo.Hk, geo.Hv, 1e-6)
+    o1 = gdn.gdn_delta_rule_step(q, k, v, g, beta, cu, st1, hi, commit_state=commit)
+    # one fused call
+    cs2, st2 = lb.conv_state.to(DEV), lb.state.to(DEV)
+    o2 = gdn.gdn_decode_fused(x, w, b, cs2, cu, g, beta, st2, geo.Hk, geo.Hv, 1e-6, hi,
+                              write_conv_state=wcs, commit_state=commit)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(st1, st2)
+    assert torch.equal(cs1, cs2)
+    if not commit:
+        assert torch.equal(st2.cpu(), lb.state)
+    if not wcs:
+        assert torch.equal(cs2.cpu(), lb.conv_state)
+
+
+def test_decode_fused_matches_oracle():
+    geo = I.Geometry(Hk=2, Hv=4)
+    lengths, hinit = [1, 4, 8, 3], [1, 0, 1, 1]
+    lb = I.make_layer(geo, lengths, "bf16", 850, state_std=0.3, has_init=hinit)
+    cu = lb.cu_seqlens.to(DEV)
+    cs, st = lb.conv_state.to(DEV), lb.state.to(DEV)
+    o = gdn.gdn_decode_fused(lb.x.to(DEV), lb.conv_w.to(DEV), None, cs, cu, lb.g.to(DEV),
+                             lb.beta.to(DEV), st, geo.Hk, geo.Hv, 1e-6, lb.has_init.to(DEV))
+    torch.cuda.synchronize()
+    hi = lb.has_init.numpy()
+    cu_l = lb.cu_seqlens.tolist()
+    y_ref, cs_ref = O.causal_conv(TL.np64(lb.x), TL.np64(lb.conv_w), None, TL.np64(lb.conv_state),
+                                  hi, cu_l, True)
+    assert np.array_equal(TL.np64(cs), cs_ref)
+    qr, kr, vr = O.postconv_l2(O.round_to_bf16(y_ref), geo.Hk, geo.Hv, 128, 128, 1e-6)
+    o_ref, st_ref = O.delta_rule_recurrent(O.round_to_bf16(qr), O.round_to_bf16(kr),
+                                           O.round_to_bf16(vr), TL.np64(lb.g), TL.np64(lb.beta),
+                                           TL.np64(lb.state), hi, cu_l, geo.Hk, geo.Hv)
+    TL.check_normwise(TL.np64(o), o_ref, TL.REC_BF16, axes=(2,), what="o")
+    TL.check_normwise(TL.np64(st), st_ref, TL.REC_BF16, axes=(2, 3), what="state")
