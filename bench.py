@@ -22,9 +22,12 @@ the dominant kernel's roofline, throughput in layer-tokens/s:
   mixed   24 layers of a serving step: 8 prefill sequences (log-uniform
           lengths in [256, 8192]) and 24 single-token decode sequences,
           6144 channels (16 q, 16 k, 16 v heads)
+  verify-fused, mixed-fused
+          the same, with the decode / draft tokens' conv, post-conv and
+          step in one fused launch per layer
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                  [--workload varlen|verify|long|mixed]
+                  [--workload varlen|verify|long|mixed|verify-fused|mixed-fused]
 """
 from __future__ import annotations
 
@@ -48,6 +51,7 @@ KERNEL_SOURCES = {
     "prefill": ["prefill.hip", "mfma.hpp", "device_common.hpp"],
     "step": ["step.hip", "mfma.hpp", "device_common.hpp"],
     "commit": ["step.hip", "mfma.hpp", "device_common.hpp"],
+    "fused": ["step.hip", "mfma.hpp", "device_common.hpp"],
 }
 STATE_BYTES = 128 * 128 * 4   # one float32 state matrix (dv x dk)
 
@@ -78,6 +82,16 @@ def recurrence_bytes(N, Hk, Hv, e, n_state_read, n_state_write):
     """q, k, v read, o written, g and beta read, plus whole float32 states."""
     return (N * (2 * Hk * 128 + Hv * 128) * e + N * Hv * 8 + N * Hv * 128 * e
             + (n_state_read + n_state_write) * Hv * STATE_BYTES)
+
+
+def fused_bytes(N, C, Hk, Hv, e, nseq, write_conv, n_state_write, kv_out):
+    """The fused decode/verify launch: x read, weights and bias slot, the
+    stored conv rows of every sequence read (and written when write_conv),
+    g and beta read, o written, every state read (and written when
+    committing), plus the kept k and v when kv_out."""
+    return (N * C * e + 20 * C + nseq * 12 * C * (2 if write_conv else 1) + N * Hv * 8
+            + N * Hv * 128 * e + (nseq + n_state_write) * Hv * STATE_BYTES
+            + (N * (Hk + Hv) * 128 * e if kv_out else 0))
 
 
 def commit_bytes(L, C, Hk, Hv, e, n_keep, nseq):
@@ -206,7 +220,7 @@ def plan_varlen(dev):
     return p
 
 
-def plan_verify(dev):
+def plan_verify(dev, fused=False):
     import torch
     from linear_attention_layers_amd import gdn, inputs
     L = 36
@@ -221,16 +235,24 @@ def plan_verify(dev):
         N, C, Hk, Hv = lb.N, lb.geo.C, lb.geo.Hk, lb.geo.Hv
         chunks = gdn.gdn_make_chunks_device(d["cu"], N)
         d["chunks"] = chunks
-        p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None, d["cu"],
-                                                         d["chunks"], False, y=d["y"]),
-              conv_bytes(N, C, 2, lb.nseq, lb.nseq, False))
-        p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"],
-                                                                         k=d["k"], v=d["v"]),
-              postconv_bytes(N, C, 2))
-        p.add("step", lambda d=d: gdn.gdn_delta_rule_step(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                                          d["cu"], d["st"], None, o=d["o"],
-                                                          commit_state=False),
-              recurrence_bytes(N, Hk, Hv, 2, lb.nseq, 0))
+        if fused:
+            # k and v are kept for the commit's replay
+            p.add("fused", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_decode_fused(
+                      d["x"], d["w"], None, d["cs"], d["cu"], d["g"], d["beta"], d["st"], Hk, Hv, 1e-6,
+                      None, o=d["o"], write_conv_state=False, commit_state=False, k_out=d["k"],
+                      v_out=d["v"]),
+                  fused_bytes(N, C, Hk, Hv, 2, lb.nseq, False, 0, True))
+        else:
+            p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None,
+                                                             d["cu"], d["chunks"], False, y=d["y"]),
+                  conv_bytes(N, C, 2, lb.nseq, lb.nseq, False))
+            p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6,
+                                                                             q=d["q"], k=d["k"], v=d["v"]),
+                  postconv_bytes(N, C, 2))
+            p.add("step", lambda d=d: gdn.gdn_delta_rule_step(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                              d["cu"], d["st"], None, o=d["o"],
+                                                              commit_state=False),
+                  recurrence_bytes(N, Hk, Hv, 2, lb.nseq, 0))
         p.keep.append(d)
         table_layers.append(dict(x=d["x"], conv_state=d["cs"], state=d["st"], k=d["k"], v=d["v"],
                                  g=d["g"], beta=d["beta"]))
@@ -242,7 +264,8 @@ def plan_verify(dev):
     p.add("commit", lambda: gdn.gdn_commit(table, L, cu0, nk, None, C, Hk, Hv, torch.bfloat16),
           commit_bytes(L, C, Hk, Hv, 2, n_keep, len(lengths)))
     p.tokens = L * sum(lengths)
-    p.config = {"workload": "spec_verify_36L_bf16", "nseq": len(lengths), "tokens": sum(lengths),
+    p.config = {"workload": "spec_verify_36L_bf16" + ("_fused" if fused else ""),
+                "nseq": len(lengths), "tokens": sum(lengths),
                 "kept_tokens": sum(n_keep), "channels": C, "Hk": Hk, "Hv": Hv, "head_dim": 128,
                 "layers": L, "state_dtype": "f32", "seed": 3000}
     return p
@@ -271,7 +294,7 @@ def plan_long(dev):
     return p
 
 
-def plan_mixed(dev):
+def plan_mixed(dev, fused=False):
     from linear_attention_layers_amd import gdn, inputs
     L = 24
     p = Plan()
@@ -285,29 +308,51 @@ def plan_mixed(dev):
         d["chunks"] = gdn.gdn_make_chunks_device(d["cu"], N)
         d["cu_pre"] = d["cu"][:npre + 1]
         d["cu_dec"] = (d["cu"][npre:] - Npre).contiguous()
-        p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None, d["cu"],
-                                                         d["chunks"], True, y=d["y"]),
-              conv_bytes(N, C, 2, lb.nseq, lb.nseq, True))
-        p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"],
-                                                                         k=d["k"], v=d["v"]),
-              postconv_bytes(N, C, 2))
+        if fused:
+            # conv and post-conv over the prefill tokens only; the decode
+            # tokens go through the fused launch
+            d["chunks_pre"] = gdn.gdn_make_chunks_device(d["cu_pre"], Npre)
+            p.add("conv", lambda d=d, n=Npre, m=npre: gdn.gdn_causal_conv_fwd(
+                      d["x"][:n], d["w"], None, d["cs"][:m], None, d["cu_pre"], d["chunks_pre"], True,
+                      y=d["y"][:n]),
+                  conv_bytes(Npre, C, 2, npre, npre, True))
+            p.add("postconv", lambda d=d, n=Npre, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(
+                      d["y"][:n], Hk, Hv, 1e-6, q=d["q"][:n], k=d["k"][:n], v=d["v"][:n]),
+                  postconv_bytes(Npre, C, 2))
+        else:
+            p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None,
+                                                             d["cu"], d["chunks"], True, y=d["y"]),
+                  conv_bytes(N, C, 2, lb.nseq, lb.nseq, True))
+            p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6,
+                                                                             q=d["q"], k=d["k"], v=d["v"]),
+                  postconv_bytes(N, C, 2))
         p.add("prefill", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_prefill(
                   d["q"][:n], d["k"][:n], d["v"][:n], d["g"][:n], d["beta"][:n], d["cu_pre"],
                   d["st"][:m], None, o=d["o"][:n]),
               recurrence_bytes(Npre, Hk, Hv, 2, npre, npre), 11.0 * 128 * 128 * Npre * Hv)
-        p.add("step", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_step(
-                  d["q"][n:], d["k"][n:], d["v"][n:], d["g"][n:], d["beta"][n:], d["cu_dec"],
-                  d["st"][m:], None, o=d["o"][n:], commit_state=True),
-              recurrence_bytes(N - Npre, Hk, Hv, 2, ndec, ndec))
+        if fused:
+            p.add("fused", lambda d=d, n=Npre, m=npre, Hk=Hk, Hv=Hv: gdn.gdn_decode_fused(
+                      d["x"][n:], d["w"], None, d["cs"][m:], d["cu_dec"], d["g"][n:], d["beta"][n:],
+                      d["st"][m:], Hk, Hv, 1e-6, None, o=d["o"][n:], write_conv_state=True,
+                      commit_state=True),
+                  fused_bytes(N - Npre, C, Hk, Hv, 2, ndec, True, ndec, False))
+        else:
+            p.add("step", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_step(
+                      d["q"][n:], d["k"][n:], d["v"][n:], d["g"][n:], d["beta"][n:], d["cu_dec"],
+                      d["st"][m:], None, o=d["o"][n:], commit_state=True),
+                  recurrence_bytes(N - Npre, Hk, Hv, 2, ndec, ndec))
         p.keep.append(d)
         p.tokens += N
-        p.config = {"workload": "mixed_serving_24L_bf16", "prefill_seqs": npre, "decode_seqs": ndec,
+        p.config = {"workload": "mixed_serving_24L_bf16" + ("_fused" if fused else ""),
+                    "prefill_seqs": npre, "decode_seqs": ndec,
                     "tokens_per_layer": N, "channels": C, "Hk": Hk, "Hv": Hv, "head_dim": 128,
                     "layers": L, "state_dtype": "f32", "seed": 5000}
     return p
 
 
-PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed}
+PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed,
+         "verify-fused": lambda dev: plan_verify(dev, fused=True),
+         "mixed-fused": lambda dev: plan_mixed(dev, fused=True)}
 
 
 def main():
@@ -326,7 +371,8 @@ def main():
               "(the GDN hot path shards by sequence and head group with no exchange; "
               "multi-GPU runs are not part of this build)", file=sys.stderr)
         sys.exit(2)
-    default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 10}[args.workload]
+    default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 10, "verify-fused": 20,
+                     "mixed-fused": 10}[args.workload]
     steps = args.steps if args.steps is not None else default_steps
     warmup = args.warmup if args.warmup is not None else max(2, steps // 10)
 

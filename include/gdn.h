@@ -236,14 +236,19 @@ int gdn_commit(const gdn_layer_io* layers, int L, const int32_t* cu_seqlens,
  * 3226") keep as separate verify-forward launches.
  *   x, x_row_stride, w, bias, conv_state: as gdn_causal_conv_fwd
  *   g, beta, state, has_initial_state, o: as gdn_delta_rule_step
+ *   k_out, v_out (device, optional, NULL = not written) [N, Hk, dk] and
+ *       [N, Hv, dv] in the activation dtype, 16-byte aligned: the normalised
+ *       k and the v of every token, bitwise equal to gdn_postconv_l2's k and
+ *       v, for a later gdn_commit of a verify window (its replay reads them).
  *   Hv must equal Hk or 2*Hk (GDN_ERR_SHAPE otherwise); eps > 0.
- *   o, state and conv_state must not overlap x or each other. */
+ *   o, k_out, v_out, state and conv_state must not overlap x or each other. */
 int gdn_decode_fused(const void* x, int64_t x_row_stride, int act,
                      const float* w, const float* bias, float* conv_state,
                      const int32_t* cu_seqlens, int nseq, int N,
                      int Hk, int Hv, int dk, int dv, float eps,
                      const float* g, const float* beta, float* state,
                      const uint8_t* has_initial_state, void* o,
+                     void* k_out, void* v_out,
                      int write_conv_state, int commit_state, void* stream);
 
 #ifdef __cplusplus

@@ -202,8 +202,8 @@ int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act, co
 int gdn_decode_fused(const void* x, int64_t xs, int act, const float* w, const float* bias,
                      float* conv_state, const int32_t* cu, int nseq, int N, int Hk, int Hv, int dk,
                      int dv, float eps, const float* g, const float* beta, float* state,
-                     const uint8_t* has_init, void* o, int write_conv_state, int commit_state,
-                     void* stream) {
+                     const uint8_t* has_init, void* o, void* k_out, void* v_out,
+                     int write_conv_state, int commit_state, void* stream) {
   if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
   if (nseq < 0 || N < 0) return fail(GDN_ERR_SHAPE, "negative nseq or N");
   int st = check_heads(Hk, Hv, dk, dv);
@@ -217,15 +217,22 @@ int gdn_decode_fused(const void* x, int64_t xs, int act, const float* w, const f
     return fail(GDN_ERR_NULL, "x, w, conv_state, cu_seqlens, g, beta, state and o are required");
   const size_t e = elem_bytes(act);
   if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || (bias && !aligned16(bias)) ||
-      !aligned16(conv_state) || !aligned16(state) || !aligned16(o))
-    return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state, state and o must be 16-byte aligned");
+      !aligned16(conv_state) || !aligned16(state) || !aligned16(o) || (k_out && !aligned16(k_out)) ||
+      (v_out && !aligned16(v_out)))
+    return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state, state, o, k_out and v_out must be 16-byte aligned");
   const size_t nx = ((size_t)(N - 1) * xs + C) * e, ncs = (size_t)nseq * 3 * C * 4;
   const size_t no = (size_t)N * Hv * dv * e, ns = (size_t)nseq * Hv * dv * dk * 4;
-  if (overlaps(o, no, x, nx) || overlaps(o, no, conv_state, ncs) || overlaps(o, no, state, ns) ||
-      overlaps(state, ns, x, nx) || overlaps(state, ns, conv_state, ncs) || overlaps(conv_state, ncs, x, nx))
-    return fail(GDN_ERR_ALIAS, "o, state and conv_state must not overlap x or each other");
+  const size_t nk = k_out ? (size_t)N * Hk * dk * e : 0, nv = v_out ? (size_t)N * Hv * dv * e : 0;
+  struct Buf { const void* p; size_t n; } out[5] = {{o, no}, {state, ns}, {conv_state, ncs}, {k_out, nk}, {v_out, nv}};
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(out[i].p, out[i].n, x, nx))
+      return fail(GDN_ERR_ALIAS, "o, k_out, v_out, state and conv_state must not overlap x or each other");
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
+        return fail(GDN_ERR_ALIAS, "o, k_out, v_out, state and conv_state must not overlap x or each other");
+  }
   return launched(gdn::launch_decode_fused(x, xs, act, w, bias, conv_state, cu, nseq, Hk, Hv, eps, g, beta,
-                                           state, has_init, o, write_conv_state, commit_state,
+                                           state, has_init, o, k_out, v_out, write_conv_state, commit_state,
                                            as_stream(stream)),
                   "decode_fused");
 }

@@ -29,7 +29,8 @@ hipError_t launch_step(const void* q, const void* k, const void* v, int act, con
 hipError_t launch_decode_fused(const void* x, int64_t xs, int act, const float* w, const float* bias,
                                float* conv_state, const int32_t* cu, int nseq, int Hk, int Hv, float eps,
                                const float* g, const float* beta, float* state, const uint8_t* has_init,
-                               void* o, int write_conv_state, int commit_state, hipStream_t st);
+                               void* o, void* k_out, void* v_out, int write_conv_state, int commit_state,
+                               hipStream_t st);
 hipError_t launch_commit(const gdn_layer_io* layers, int L, const int32_t* cu,
                          const int32_t* n_keep, const uint8_t* has_init, int nseq, int C,
                          int Hk, int Hv, int act, hipStream_t st);

@@ -366,7 +366,8 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
     float* conv_state, const int32_t* __restrict__ cu, int Hk, int Hv, float eps,
     const float* __restrict__ g, const float* __restrict__ beta, float* state,
-    const uint8_t* __restrict__ has_init, T* __restrict__ o, int write_conv_state, int commit_state) {
+    const uint8_t* __restrict__ has_init, T* __restrict__ o, T* __restrict__ k_out, T* __restrict__ v_out,
+    int write_conv_state, int commit_state) {
   using PR = Prec<T>;
   using E = typename PR::E;
   constexpr int LDK = FusedSmem<T, G>::LDK;
@@ -448,6 +449,12 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
       }
       E* dst = hd == 0 ? sm.Qs : hd == 1 ? sm.Ks : sm.Vs[hd - 2];
       Act<T>::store8(dst + tok * LDK + 8 * jl, out);
+      // the normalised k and the v kept for a later commit's replay
+      if (tok < n) {
+        const int64_t t = (int64_t)bos + c0 + tok;
+        if (hd == 1 && k_out != nullptr) Act<T>::store8(k_out + (t * Hk + kh) * 128 + 8 * jl, out);
+        if (hd >= 2 && v_out != nullptr) Act<T>::store8(v_out + (t * Hv + kh * G + hd - 2) * 128 + 8 * jl, out);
+      }
     }
     __syncthreads();
 
@@ -606,13 +613,14 @@ hipError_t launch_step(const void* q, const void* k, const void* v, int act, con
 hipError_t launch_decode_fused(const void* x, int64_t xs, int act, const float* w, const float* bias,
                                float* conv_state, const int32_t* cu, int nseq, int Hk, int Hv, float eps,
                                const float* g, const float* beta, float* state, const uint8_t* has_init,
-                               void* o, int write_conv_state, int commit_state, hipStream_t st) {
+                               void* o, void* k_out, void* v_out, int write_conv_state, int commit_state,
+                               hipStream_t st) {
   const int G = Hv / Hk;
   const dim3 grid(nseq * Hk);
 #define GDN_FUSED_LAUNCH(TT, GG)                                                                   \
   hipLaunchKernelGGL((fused_kernel<TT, GG>), grid, dim3(256 * GG), 0, st, static_cast<const TT*>(x), xs, w, \
                      bias, conv_state, cu, Hk, Hv, eps, g, beta, state, has_init, static_cast<TT*>(o),     \
-                     write_conv_state, commit_state)
+                     static_cast<TT*>(k_out), static_cast<TT*>(v_out), write_conv_state, commit_state)
   if (act == GDN_F32) {
     if (G == 1) GDN_FUSED_LAUNCH(float, 1);
     else GDN_FUSED_LAUNCH(float, 2);

@@ -82,7 +82,8 @@ _step = _sig("gdn_delta_rule_step", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _
 _commit = _sig("gdn_commit", [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                               _vp])
 _decode_fused = _sig("gdn_decode_fused", [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                          _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _vp])
+                                          _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                          _vp])
 
 EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
             "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd",
@@ -268,8 +269,11 @@ def gdn_delta_rule_step(q, k, v, g, beta, cu_seqlens, state, has_initial_state=N
 def gdn_decode_fused(x, w, bias, conv_state, cu_seqlens, g, beta, state, Hk: int, Hv: int,
                      eps: float = 1e-6, has_initial_state=None, o: Optional[torch.Tensor] = None,
                      write_conv_state: bool = True, commit_state: bool = True,
+                     k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
-    """conv + post-conv + step in one launch (bitwise equal to the three calls)."""
+    """conv + post-conv + step in one launch (bitwise equal to the three calls).
+    k_out [N, Hk, 128] / v_out [N, Hv, 128] (optional, activation dtype)
+    receive the normalised k and the v for a later gdn_commit."""
     N, C = x.shape
     _require(x.stride(1) == 1, "x rows must be contiguous")
     for t, nm in ((w, "w"), (conv_state, "conv_state"), (g, "g"), (beta, "beta"), (state, "state")):
@@ -281,10 +285,15 @@ def gdn_decode_fused(x, w, bias, conv_state, cu_seqlens, g, beta, state, Hk: int
     if o is None:
         o = torch.empty(N, Hv, 128, dtype=x.dtype, device=x.device)
     _dense(o, "o")
+    for t, nm, H in ((k_out, "k_out", Hk), (v_out, "v_out", Hv)):
+        if t is not None:
+            _dense(t, nm)
+            _require(t.dtype == x.dtype and t.numel() == N * H * 128, f"{nm}: [N, {H}, 128] of x's dtype")
     nseq = cu_seqlens.numel() - 1
     _check(_decode_fused(_ptr(x), x.stride(0), _code(x.dtype), _ptr(w), _ptr(bias), _ptr(conv_state),
                          _ptr(cu_seqlens), nseq, N, Hk, Hv, 128, 128, float(eps), _ptr(g), _ptr(beta),
-                         _ptr(state), _ptr(has_initial_state), _ptr(o), int(bool(write_conv_state)),
+                         _ptr(state), _ptr(has_initial_state), _ptr(o), _ptr(k_out), _ptr(v_out),
+                         int(bool(write_conv_state)),
                          int(bool(commit_state)), _stream(stream)), "gdn_decode_fused")
     return o
 

@@ -187,19 +187,19 @@ def test_decode_fused_validation():
     fn = lib.gdn_decode_fused
     fn.restype = i32
     fn.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp,
-                   vp, i32, i32, vp]
+                   vp, vp, vp, i32, i32, vp]
     Hk, Hv = 2, 4
     C = 2 * Hk * 128 + Hv * 128
     base = dict(x=FAKE, xs=C, act=1, w=FAKE + (1 << 24), bias=None, cs=FAKE + (2 << 24),
                 cu=FAKE + (3 << 24), nseq=2, N=10, Hk=Hk, Hv=Hv, dk=128, dv=128, eps=1e-6,
                 g=FAKE + (4 << 24), beta=FAKE + (5 << 24), st=FAKE + (6 << 24), hi=None,
-                o=FAKE + (8 << 24), wcs=1, commit=1)
+                o=FAKE + (8 << 24), ko=None, vo=None, wcs=1, commit=1)
 
     def call(**kw):
         a = dict(base, **kw)
         return fn(a["x"], a["xs"], a["act"], a["w"], a["bias"], a["cs"], a["cu"], a["nseq"], a["N"],
                   a["Hk"], a["Hv"], a["dk"], a["dv"], a["eps"], a["g"], a["beta"], a["st"], a["hi"],
-                  a["o"], a["wcs"], a["commit"], None)
+                  a["o"], a["ko"], a["vo"], a["wcs"], a["commit"], None)
 
     assert call(Hv=8) == SHAPE             # only Hv = Hk or 2 Hk
     assert call(Hv=3) == SHAPE
@@ -212,5 +212,9 @@ def test_decode_fused_validation():
     assert call(o=FAKE + (8 << 24) + 4) == ALIGN
     assert call(o=FAKE + 64) == ALIAS      # o inside x
     assert call(cs=FAKE + (6 << 24) + 64) == ALIAS   # conv_state inside state
+    assert call(ko=FAKE + (9 << 24) + 2) == ALIGN
+    assert call(ko=FAKE + (8 << 24) + 256) == ALIAS   # k_out inside o
+    assert call(vo=FAKE + (9 << 24), ko=FAKE + (9 << 24) + 4096) == ALIAS   # k_out inside v_out
+    assert call(vo=FAKE + 128) == ALIAS     # v_out inside x
     assert call(N=0) == OK                 # empty: no launch
     assert call(nseq=0) == OK

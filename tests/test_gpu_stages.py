@@ -447,10 +447,15 @@ def test_decode_fused_bitwise_equal_to_three_calls(case):
     o1 = gdn.gdn_delta_rule_step(q, k, v, g, beta, cu, st1, hi, commit_state=commit)
     # one fused call
     cs2, st2 = lb.conv_state.to(DEV), lb.state.to(DEV)
+    keep_kv = case % 2 == 0
+    k2 = torch.full_like(k, float("nan")) if keep_kv else None
+    v2 = torch.full_like(v, float("nan")) if keep_kv else None
     o2 = gdn.gdn_decode_fused(x, w, b, cs2, cu, g, beta, st2, geo.Hk, geo.Hv, 1e-6, hi,
-                              write_conv_state=wcs, commit_state=commit)
+                              write_conv_state=wcs, commit_state=commit, k_out=k2, v_out=v2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+    if keep_kv:
+        assert torch.equal(k, k2) and torch.equal(v, v2)
     assert torch.equal(st1, st2)
     assert torch.equal(cs1, cs2)
     if not commit:

@@ -226,3 +226,66 @@ def test_mixed_serving_24_layers_sampled():
             _check_postconv_tokens(lb, out, list(range(0, lb.N, 53)) + list(range(Npre, lb.N)))
             for heads in ([0], [15]):
                 _check_recurrence(lb, out, heads, TL.REC_BF16)
+
+
+def test_spec_verify_fused_then_commit_bitwise_equal_to_unfused():
+    """The verify window through the fused launch (k and v kept for the
+    replay), then one commit: bitwise the same o, state and conv_state as
+    conv + post-conv + step, then the same commit."""
+    L = 4
+    lengths, n_keep = I.spec_verify_window()
+    res = {}
+    for fused in (False, True):
+        layers, outs = [], []
+        for layer in range(L):
+            lb = I.spec_verify_layer(layer)
+            cu = lb.cu_seqlens.to(DEV)
+            cs, st = lb.conv_state.to(DEV), lb.state.to(DEV)
+            x, w = lb.x.to(DEV), lb.conv_w.to(DEV)
+            g, beta = lb.g.to(DEV), lb.beta.to(DEV)
+            Hk, Hv = lb.geo.Hk, lb.geo.Hv
+            if fused:
+                k = torch.empty(lb.N, Hk, 128, dtype=x.dtype, device=DEV)
+                v = torch.empty(lb.N, Hv, 128, dtype=x.dtype, device=DEV)
+                o = gdn.gdn_decode_fused(x, w, None, cs, cu, g, beta, st, Hk, Hv, 1e-6, None,
+                                         write_conv_state=False, commit_state=False, k_out=k, v_out=v)
+            else:
+                y = gdn.gdn_causal_conv_fwd(x, w, None, cs, None, cu,
+                                            gdn.gdn_make_chunks_device(cu, lb.N), False)
+                q, k, v = gdn.gdn_postconv_l2(y, Hk, Hv, 1e-6)
+                o = gdn.gdn_delta_rule_step(q, k, v, g, beta, cu, st, None, commit_state=False)
+            outs.append((o, st, cs))
+            layers.append(dict(x=x, conv_state=cs, state=st, k=k, v=v, g=g, beta=beta))
+        table = gdn.gdn_layer_table(layers, DEV)
+        lb0 = I.spec_verify_layer(0)
+        gdn.gdn_commit(table, L, lb0.cu_seqlens.to(DEV), lb0.n_keep.to(DEV), None, lb0.geo.C,
+                       lb0.geo.Hk, lb0.geo.Hv, torch.bfloat16)
+        torch.cuda.synchronize()
+        res[fused] = [tuple(t.cpu() for t in r) for r in outs]
+    for layer in range(L):
+        for a, b, nm in zip(res[False][layer], res[True][layer], ("o", "state", "conv_state")):
+            assert torch.equal(a, b), f"layer {layer} {nm}"
+
+
+def test_mixed_serving_fused_decode_bitwise_equal_to_unfused():
+    lb = I.mixed_serving_layer(0)
+    npre = lb.meta["n_prefill"]
+    Npre = int(lb.cu_seqlens[npre])
+    Hk, Hv = lb.geo.Hk, lb.geo.Hv
+    cu = lb.cu_seqlens.to(DEV)
+    cu_dec = (cu[npre:] - Npre).contiguous()
+    x, w = lb.x.to(DEV), lb.conv_w.to(DEV)
+    g, beta = lb.g.to(DEV), lb.beta.to(DEV)
+    # unfused decode part: conv over every token, step over the decode tokens
+    cs1, st1 = lb.conv_state.to(DEV), lb.state.to(DEV)
+    y = gdn.gdn_causal_conv_fwd(x, w, None, cs1, None, cu, gdn.gdn_make_chunks_device(cu, lb.N), True)
+    q, k, v = gdn.gdn_postconv_l2(y, Hk, Hv, 1e-6)
+    o1 = gdn.gdn_delta_rule_step(q[Npre:], k[Npre:], v[Npre:], g[Npre:], beta[Npre:], cu_dec,
+                                 st1[npre:], None, commit_state=True)
+    cs2, st2 = lb.conv_state.to(DEV), lb.state.to(DEV)
+    o2 = gdn.gdn_decode_fused(x[Npre:], w, None, cs2[npre:], cu_dec, g[Npre:], beta[Npre:],
+                              st2[npre:], Hk, Hv, 1e-6, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(st1[npre:], st2[npre:])
+    assert torch.equal(cs1[npre:], cs2[npre:])
