@@ -247,7 +247,7 @@ int gdn_commit(const gdn_layer_io* layers, int L, const int32_t* cu, const int32
   if (C != 2 * Hk * dk + Hv * dv) return fail(GDN_ERR_SHAPE, "C must equal 2*Hk*dk + Hv*dv");
   if (L == 0 || nseq == 0) return GDN_OK;
   if (!layers || !cu || !n_keep) return fail(GDN_ERR_NULL, "layers, cu_seqlens and n_keep are required");
-  const long long blocks = (long long)L * nseq * (Hv + (C + 2047) / 2048);
+  const long long blocks = (long long)L * nseq * (Hv + (C + 1023) / 1024);
   if (blocks > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "too many (layer, sequence) pairs");
   return launched(gdn::launch_commit(layers, L, cu, n_keep, has_init, nseq, C, Hk, Hv, act,
                                      as_stream(stream)),

@@ -27,13 +27,16 @@
 // triangular inverse.  The kernel is then bound by reading (and, when
 // committing, writing) the float32 state.
 //
-// Layout.  One workgroup of 4 waves per (sequence, v-head); wave w owns
-// state rows 32 w .. 32 w + 31 as two 16-row blocks, held TRANSPOSED in
-// MFMA accumulators (the prefill's layout).  Every wave loads the block's K
-// and Q fragments itself and keeps its own LDS scratch, so there is no
-// barrier.  The commit replays the kept tokens through the same function,
-// so its state is bitwise equal to the state a committing step over those
-// tokens writes.
+// Layout.  One workgroup of 2 waves per (sequence, v-head); wave w owns
+// state rows 64 w .. 64 w + 63 as four 16-row blocks, held TRANSPOSED in
+// MFMA accumulators (the prefill's layout).  At two waves per SIMD every
+// workgroup of a 32-sequence x 32-head launch is resident at once, so all
+// state reads are in flight together instead of in two rounds.  Each wave
+// loads half of the block's K and Q rows and stages it in LDS (one barrier
+// per block); fragments are read back from LDS where they are used, and
+// each wave keeps its own scratch for the inverse.  The commit replays the
+// kept tokens through the same function, so its state is bitwise equal to
+// the state a committing step over those tokens writes.
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -41,19 +44,32 @@ namespace gdn {
 
 namespace {
 
-constexpr int kStepThreads = 256;
+constexpr int kStepWaves = 2;                  // waves per (sequence, v-head)
+constexpr int kStepThreads = 64 * kStepWaves;
+constexpr int kRB = 128 / 16 / kStepWaves;     // 16-row state blocks per wave
+constexpr int kRows = 16 * kRB;                // state rows per wave
+constexpr int kSlices = 4 / kStepWaves;        // 32-column K / Q slices each wave stages
 constexpr int kWin = 16;     // tokens per block of a window
 constexpr float kLog2e = 1.4426950408889634f;
 
+// One wave's scratch for a block.
+template <class T> struct WaveScratch {
+  using E = typename Prec<T>::E;
+  static constexpr int LDT = kWin + Prec<T>::PAD;  // rows of T = (I + A)^-1
+  E Tm[kWin * LDT];
+  float A[kWin][20];
+  float W[4][64];           // log2-scaled L, gamma, beta, d of the block's tokens (entries
+                            // past 16 are written by the other lanes and never read)
+};
+
+// The block's K and Q rows, shared by the workgroup's waves (each wave
+// stages one 32-column slice), and every wave's scratch.
 template <class T> struct StepSmem {
   using E = typename Prec<T>::E;
-  static constexpr int LDK = 128 + Prec<T>::PAD;   // K rows of the block
-  static constexpr int LDT = kWin + Prec<T>::PAD;  // rows of T = (I + A)^-1
-  E K[4][kWin * LDK];
-  E Tm[4][kWin * LDT];
-  float A[4][kWin][20];
-  float W[4][4][64];        // log2-scaled L, gamma, beta, d of the block's tokens (entries
-                            // past 16 are written by the other lanes and never read)
+  static constexpr int LDK = 128 + Prec<T>::PAD;
+  E K[kWin * LDK];
+  E Q[kWin * LDK];
+  WaveScratch<T> w[kStepWaves];
 };
 
 // S^T of rows v0 + 16 b + r16 in accumulator layout: tile cb holds
@@ -61,38 +77,40 @@ template <class T> struct StepSmem {
 // that spans the state, or nothing (all zeros) when there is no initial
 // state, so the read is branch-free.
 __device__ __forceinline__ void load_state(const float* base, bool init, int v0, int r16, int kg,
-                                           f32x4 (&st)[2][8]) {
+                                           f32x4 (&st)[kRB][8]) {
   const auto rs = buf_rsrc(base, init ? 128 * 128 * 4 : 0);
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < kRB; ++b)
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
       st[b][cb] = __builtin_bit_cast(
           f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((v0 + 16 * b + r16) * 128 + 16 * cb + 4 * kg) * 4, 0, 0));
 }
 
-__device__ __forceinline__ void store_state(float* base, int v0, int r16, int kg, const f32x4 (&st)[2][8]) {
+__device__ __forceinline__ void store_state(float* base, int v0, int r16, int kg, const f32x4 (&st)[kRB][8]) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < kRB; ++b)
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
       *reinterpret_cast<float4*>(base + (v0 + 16 * b + r16) * 128 + 16 * cb + 4 * kg) =
           make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
 }
 
-// Token inputs of one block of a window, in registers.
+// Token inputs of one block of a window, in registers: this wave's
+// 32-column slice of the K and Q rows (staged to LDS for every wave), and
+// what the wave alone reads.
 template <class T, bool WITH_O> struct BlockIn {
-  typename Prec<T>::F32 kf[4], qf[4];   // K, Q fragments (token r16)
-  float vv[2][4];                       // V (token 4 kg + e, state row v0 + 16 b + r16)
+  typename Prec<T>::F32 kf[kSlices], qf[kSlices];   // K, Q slice fragments (token r16)
+  float vv[kRB][4];                     // V (token 4 kg + e, state row v0 + 16 b + r16)
   float gl, bl;                         // log a, beta of token `lane` (lanes < 16)
   int n;
   int64_t t0;
 };
 
 template <class T, bool WITH_O>
-__device__ __forceinline__ void load_block(BlockIn<T, WITH_O>& in, int lane, const T* q, const T* k,
-                                           const T* v, const float* g, const float* beta, int64_t t0,
-                                           int n, int Hk, int Hv, int h, int kh, int v0) {
+__device__ __forceinline__ void load_block(BlockIn<T, WITH_O>& in, int lane, int wave, const T* q,
+                                           const T* k, const T* v, const float* g, const float* beta,
+                                           int64_t t0, int n, int Hk, int Hv, int h, int kh, int v0) {
   using PR = Prec<T>;
   constexpr int ES = sizeof(typename PR::E);
   const int r16 = lane & 15, kg = lane >> 4;
@@ -107,33 +125,51 @@ __device__ __forceinline__ void load_block(BlockIn<T, WITH_O>& in, int lane, con
   const auto rq = buf_rsrc(q + t0 * Hk * 128, n * Hk * 128 * ES);
   const auto rv = buf_rsrc(v + t0 * Hv * 128, n * Hv * 128 * ES);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int off = ((r16 * Hk + kh) * 128 + 32 * t + 4 * kg) * ES;
-    in.kf[t] = PR::gfrag32(rk, off);
-    if (WITH_O) in.qf[t] = PR::gfrag32(rq, off);
+  for (int i = 0; i < kSlices; ++i) {
+    const int off = ((r16 * Hk + kh) * 128 + 32 * (kSlices * wave + i) + 4 * kg) * ES;
+    in.kf[i] = PR::gfrag32(rk, off);
+    if (WITH_O) in.qf[i] = PR::gfrag32(rq, off);
   }
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < kRB; ++b)
 #pragma unroll
     for (int e = 0; e < 4; ++e) in.vv[b][e] = PR::gload1(rv, (((4 * kg + e) * Hv + h) * 128 + v0 + 16 * b + r16) * ES);
 }
 
-// One block of a window: o of its tokens (WITH_O) and, when `advance`, the
-// state moved past them.
+// This wave's slices of the block's K and Q rows into the shared tiles.
 template <class T, bool WITH_O>
-__device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f32x4 (&st)[2][8],
-                                          const BlockIn<T, WITH_O>& in, T* o, int Hv, int h,
-                                          bool advance) {
+__device__ __forceinline__ void stage_block(typename Prec<T>::E* Ks, typename Prec<T>::E* Qs,
+                                            const BlockIn<T, WITH_O>& in, int wave, int lane) {
+  using PR = Prec<T>;
+  constexpr int LDK = StepSmem<T>::LDK;
+  const int r16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < kSlices; ++i) {
+    const int c = 32 * (kSlices * wave + i) + 4 * kg;
+    PR::put_frag32(Ks + r16 * LDK + c, in.kf[i]);
+    if (WITH_O) PR::put_frag32(Qs + r16 * LDK + c, in.qf[i]);
+  }
+}
+
+// One block of a window: o of its tokens (WITH_O) and, when `advance`, the
+// state moved past them.  Ks / Qs hold the block's K and Q rows (16 x 128,
+// row stride LDK); `wave` selects the state rows 32 wave .. 32 wave + 31.
+// K and Q fragments are read from the tiles where they are used, so they
+// are not held in registers next to the state.
+template <class T, bool WITH_O>
+__device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Prec<T>::E* Ks,
+                                          const typename Prec<T>::E* Qs, int wave, int lane,
+                                          f32x4 (&st)[kRB][8], const BlockIn<T, WITH_O>& in, T* o,
+                                          int Hv, int h, bool advance) {
   using PR = Prec<T>;
   using E = typename PR::E;
   constexpr int ES = sizeof(E);
-  constexpr int LDK = StepSmem<T>::LDK, LDT = StepSmem<T>::LDT;
+  constexpr int LDK = StepSmem<T>::LDK, LDT = WaveScratch<T>::LDT;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int v0 = 32 * wave;
+  const int v0 = kRows * wave;
   const int n = in.n;
-  E* Ks = sm.K[wave];
-  E* Tm = sm.Tm[wave];
-  float* Wl = &sm.W[wave][0][0];
+  E* Tm = ws.Tm;
+  float* Wl = &ws.W[0][0];
 
   // gate vectors: lane t < 16 holds token t (zero past the block's end);
   // every lane writes its slot, so the loads are never sunk into a branch
@@ -147,17 +183,14 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
     Wl[192 + lane] = lane < n ? __builtin_amdgcn_exp2f(Llast - L) : 0.f;
   }
 
-  // this wave's copy of the block's K rows, for the transposed read
-#pragma unroll
-  for (int t = 0; t < 4; ++t) PR::put_frag32(Ks + r16 * LDK + 32 * t + 4 * kg, in.kf[t]);
-
   // transposed token products: lane (r16, kg) element e holds k_j . k_i
   // and k_j . q_i for i = r16, j = 4 kg + e
   f32x4 kk = zero4(), qk = zero4();
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    kk = PR::mma32(in.kf[t], in.kf[t], kk);
-    if (WITH_O) qk = PR::mma32(in.kf[t], in.qf[t], qk);
+    const auto kf = PR::lds32(Ks, LDK, r16, 32 * t, kg);
+    kk = PR::mma32(kf, kf, kk);
+    if (WITH_O) qk = PR::mma32(kf, PR::lds32(Qs, LDK, r16, 32 * t, kg), qk);
   }
 
   // A (row i = r16, columns j = 4 kg + e) to LDS, P kept as the B operand
@@ -175,7 +208,7 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
       av[e] = j < r16 ? bi * dec * kk[e] : 0.f;
       pv[e] = dec * qk[e];
     }
-    *reinterpret_cast<float4*>(&sm.A[wave][r16][4 * kg]) = make_float4(av[0], av[1], av[2], av[3]);
+    *reinterpret_cast<float4*>(&ws.A[r16][4 * kg]) = make_float4(av[0], av[1], av[2], av[3]);
   }
 
   // T = (I + A)^-1 by forward substitution: lane (c, q) = (lane / 4,
@@ -193,7 +226,7 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
       float a4[4][4];   // A[qd + 4 m][4 j4 .. 4 j4 + 3]
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const float4 t = *reinterpret_cast<const float4*>(&sm.A[wave][qd + 4 * m][4 * j4]);
+        const float4 t = *reinterpret_cast<const float4*>(&ws.A[qd + 4 * m][4 * j4]);
         a4[m][0] = t.x; a4[m][1] = t.y; a4[m][2] = t.z; a4[m][3] = t.w;
       }
 #pragma unroll
@@ -209,17 +242,21 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
   const auto tf = PR::lds16(Tm, LDT, r16, 0, kg);
 
   // Z = K S0^T (rows: tokens) and (Q S0^T)^T (rows: state rows)
-  f32x4 z[2], qt[2];
+  f32x4 z[kRB], qt[kRB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) { z[b] = zero4(); qt[b] = zero4(); }
+  for (int b = 0; b < kRB; ++b) { z[b] = zero4(); qt[b] = zero4(); }
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 4; ++t) {
+    const auto kf = PR::lds32(Ks, LDK, r16, 32 * t, kg);
+    typename PR::F32 qf;
+    if (WITH_O) qf = PR::lds32(Qs, LDK, r16, 32 * t, kg);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kRB; ++b) {
       const auto bs = PR::reg32(st[b][2 * t], st[b][2 * t + 1]);
-      z[b] = PR::mma32(in.kf[t], bs, z[b]);
-      if (WITH_O) qt[b] = PR::mma32(bs, in.qf[t], qt[b]);
+      z[b] = PR::mma32(kf, bs, z[b]);
+      if (WITH_O) qt[b] = PR::mma32(bs, qf, qt[b]);
     }
+  }
 
   // R = diag(beta) (V - diag(gamma) Z), D = T R (rows: tokens)
   const float4 ga = *reinterpret_cast<const float4*>(&Wl[64 + 4 * kg]);
@@ -227,9 +264,9 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
   const float4 dd = *reinterpret_cast<const float4*>(&Wl[192 + 4 * kg]);
   const float gam[4] = {ga.x, ga.y, ga.z, ga.w}, bet[4] = {be.x, be.y, be.z, be.w};
   const float dec4[4] = {dd.x, dd.y, dd.z, dd.w};
-  f32x4 dl[2];
+  f32x4 dl[kRB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+  for (int b = 0; b < kRB; ++b) {
     f32x4 rr;
 #pragma unroll
     for (int e = 0; e < 4; ++e) rr[e] = bet[e] * (in.vv[b][e] - gam[e] * z[b][e]);
@@ -246,7 +283,7 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
     const auto pf = PR::reg16(f32x4{pv[0], pv[1], pv[2], pv[3]});
     const float gt = Wl[64 + r16];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kRB; ++b) {
       const f32x4 pu = PR::mma16(PR::reg16(dl[b]), pf, zero4());
       float ov[4];
 #pragma unroll
@@ -258,9 +295,9 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
   // S^T <- gamma_{n-1} S^T + K^T diag(d) D
   if (advance) {
     const float gl = __builtin_amdgcn_exp2f(Wl[n - 1]);
-    typename PR::F16 du[2];
+    typename PR::F16 du[kRB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kRB; ++b) {
       f32x4 t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[e] = dl[b][e] * dec4[e];
@@ -270,7 +307,7 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
     for (int cb = 0; cb < 8; ++cb) {
       const auto kt = PR::ldsT16(Ks, LDK, 16 * cb, lane);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < kRB; ++b) {
         f32x4 acc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = gl * st[b][cb][e];
@@ -286,23 +323,29 @@ __device__ __forceinline__ void run_block(StepSmem<T>& sm, int wave, int lane, f
 // in flight together.  WITH_O writes o; the state is advanced over every
 // block except, when !write_state, the last.
 template <class T, bool WITH_O>
-__device__ __forceinline__ void run_window(StepSmem<T>& sm, int wave, int lane, f32x4 (&st)[2][8],
+__device__ __forceinline__ void run_window(StepSmem<T>& sm, int wave, int lane, f32x4 (&st)[kRB][8],
                                            BlockIn<T, WITH_O>& in, const T* q, const T* k,
                                            const T* v, const float* g, const float* beta, T* o,
                                            int bos, int len, int Hk, int Hv, int h, int kh,
                                            bool write_state) {
-  const int v0 = 32 * wave;
-  run_block<T, WITH_O>(sm, wave, lane, st, in, o, Hv, h, write_state || len > kWin);
+  const int v0 = kRows * wave;
+  stage_block<T, WITH_O>(sm.K, sm.Q, in, wave, lane);
+  __syncthreads();
+  run_block<T, WITH_O>(sm.w[wave], sm.K, sm.Q, wave, lane, st, in, o, Hv, h, write_state || len > kWin);
   for (int c0 = kWin; c0 < len; c0 += kWin) {
-    load_block<T, WITH_O>(in, lane, q, k, v, g, beta, (int64_t)bos + c0, min(kWin, len - c0), Hk, Hv,
-                          h, kh, v0);
-    run_block<T, WITH_O>(sm, wave, lane, st, in, o, Hv, h, write_state || c0 + kWin < len);
+    load_block<T, WITH_O>(in, lane, wave, q, k, v, g, beta, (int64_t)bos + c0, min(kWin, len - c0), Hk,
+                          Hv, h, kh, v0);
+    __syncthreads();   // every wave is done with the previous block's rows
+    stage_block<T, WITH_O>(sm.K, sm.Q, in, wave, lane);
+    __syncthreads();
+    run_block<T, WITH_O>(sm.w[wave], sm.K, sm.Q, wave, lane, st, in, o, Hv, h,
+                         write_state || c0 + kWin < len);
   }
 }
 
-__device__ __forceinline__ void zero_state(f32x4 (&st)[2][8]) {
+__device__ __forceinline__ void zero_state(f32x4 (&st)[kRB][8]) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < kRB; ++b)
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) st[b][cb] = zero4();
 }
@@ -311,7 +354,7 @@ __device__ __forceinline__ void zero_state(f32x4 (&st)[2][8]) {
 // right after the first block's token inputs (a state without an initial
 // value is read and then discarded), so no load waits on the flag.
 template <class T>
-__global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 3 : 2) void step_kernel(
+__global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
     int Hk, int Hv, float* state, const uint8_t* __restrict__ has_init, T* __restrict__ o,
@@ -323,14 +366,14 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 3 : 2) void step_ker
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
-  const int v0 = 32 * wave;
+  const int v0 = kRows * wave;
   const int bos = cu[s], len = cu[s + 1] - bos;
   if (len <= 0) return;
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
   const bool init = has_init == nullptr || has_init[s] != 0;
   BlockIn<T, true> in;
-  load_block<T, true>(in, lane, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
-  f32x4 st[2][8];
+  load_block<T, true>(in, lane, wave, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
+  f32x4 st[kRB][8];
   load_state(base, true, v0, r16, kg, st);
   if (!init) zero_state(st);
   run_window<T, true>(sm, wave, lane, st, in, q, k, v, g, beta, o, bos, len, Hk, Hv, h, kh,
@@ -342,7 +385,7 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 3 : 2) void step_ker
 // Fused decode / verify step: the causal conv over the window's x rows, SiLU,
 // the q / k L2 norm and the step in one launch, with y, q, k and v kept on
 // chip.  One workgroup per (sequence, k-head) holds the G = Hv / Hk v-heads
-// that read that k-head (4 waves each), so it owns every channel it reads:
+// that read that k-head (2 waves each), so it owns every channel it reads:
 // q and k of the k-head and v of its v-heads.  Its optional in-place
 // conv_state update therefore cannot race with another workgroup.
 //
@@ -355,14 +398,14 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 3 : 2) void step_ker
 template <class T, int G> struct FusedSmem {
   using E = typename Prec<T>::E;
   static constexpr int LDK = 128 + Prec<T>::PAD;
-  StepSmem<T> step[G];
+  WaveScratch<T> w[kStepWaves * G];
   E Qs[kWin * LDK];
   E Ks[kWin * LDK];
   E Vs[G][kWin * LDK];
 };
 
 template <class T, int G>
-__global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
+__global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fused_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
     float* conv_state, const int32_t* __restrict__ cu, int Hk, int Hv, float eps,
     const float* __restrict__ g, const float* __restrict__ beta, float* state,
@@ -375,9 +418,9 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
   const int s = blockIdx.x / Hk, kh = blockIdx.x % Hk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wl = wave & 3;
+  const int grp = wave / kStepWaves, wl = wave % kStepWaves;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int v0 = 32 * wl;
+  const int v0 = kRows * wl;
   const int h = kh * G + grp;
   const int C = (2 * Hk + Hv) * 128;
   const int bos = cu[s], len = cu[s + 1] - bos;
@@ -385,7 +428,7 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
   const bool init = has_init == nullptr || has_init[s] != 0;
   float* cs = conv_state + (int64_t)s * 3 * C;
 
-  f32x4 st[2][8];
+  f32x4 st[kRB][8];
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
   load_state(base, true, v0, r16, kg, st);
   if (!init) zero_state(st);
@@ -398,7 +441,7 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
   };
   for (int c0 = 0; c0 < len; c0 += kWin) {
     const int n = min(kWin, len - c0);
-    for (int unit = row; unit < kWin * (2 + G); unit += 16 * G) {
+    for (int unit = row; unit < kWin * (2 + G); unit += kStepThreads * G / 16) {
       const int tok = unit % kWin, hd = unit / kWin;
       const int ch = channel(hd);
       float out[8];
@@ -458,17 +501,12 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
     }
     __syncthreads();
 
-    // phase B: the step's block on this v-head group's 4 waves
-    BlockIn<T, true> in;
+    // phase B: the step's block on this v-head group's waves
+    BlockIn<T, true> in;   // K and Q are read from the tiles
     in.n = n;
     in.t0 = (int64_t)bos + c0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      in.kf[t] = PR::lds32(sm.Ks, LDK, r16, 32 * t, kg);
-      in.qf[t] = PR::lds32(sm.Qs, LDK, r16, 32 * t, kg);
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kRB; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) in.vv[b][e] = PR::to_f32(sm.Vs[grp][(4 * kg + e) * LDK + v0 + 16 * b + r16]);
     {
@@ -478,7 +516,8 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
       in.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
       in.bl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, goff, 0, 0));
     }
-    run_block<T, true>(sm.step[grp], wl, lane, st, in, o, Hv, h, commit_state != 0 || c0 + kWin < len);
+    run_block<T, true>(sm.w[wave], sm.Ks, sm.Qs, wl, lane, st, in, o, Hv, h,
+                       commit_state != 0 || c0 + kWin < len);
     __syncthreads();
   }
   if (commit_state) store_state(base, v0, r16, kg, st);
@@ -516,10 +555,10 @@ __global__ __launch_bounds__(256 * G, G == 1 ? 2 : 1) void fused_kernel(
 
 // One launch for all layers: block b covers (layer, sequence, role); roles
 // 0..Hv-1 replay the state of v-head `role`, roles Hv.. shift the conv rows
-// of one 2048-channel group.  A block whose sequence keeps no token exits
+// of one group of 8 * kStepThreads channels.  A block whose sequence keeps no token exits
 // before touching memory.
 template <class T>
-__global__ __launch_bounds__(kStepThreads, 2) void commit_kernel(
+__global__ __launch_bounds__(kStepThreads, 1) void commit_kernel(
     const gdn_layer_io* __restrict__ layers, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ n_keep, const uint8_t* __restrict__ has_init, int nseq, int C,
     int Hk, int Hv, int roles) {
@@ -540,15 +579,15 @@ __global__ __launch_bounds__(kStepThreads, 2) void commit_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r16 = lane & 15, kg = lane >> 4;
     float* base = io.state + ((int64_t)s * Hv + h) * (128 * 128);
-    f32x4 st[2][8];
+    f32x4 st[kRB][8];
     BlockIn<T, false> in;
-    load_block<T, false>(in, lane, nullptr, static_cast<const T*>(io.k), static_cast<const T*>(io.v), io.g,
-                         io.beta, bos, min(kWin, n), Hk, Hv, h, kh, 32 * wave);
-    load_state(base, init, 32 * wave, r16, kg, st);
+    load_block<T, false>(in, lane, wave, nullptr, static_cast<const T*>(io.k), static_cast<const T*>(io.v), io.g,
+                         io.beta, bos, min(kWin, n), Hk, Hv, h, kh, kRows * wave);
+    load_state(base, init, kRows * wave, r16, kg, st);
     run_window<T, false>(sm, wave, lane, st, in, nullptr, static_cast<const T*>(io.k),
                          static_cast<const T*>(io.v), io.g, io.beta, nullptr, bos, n, Hk, Hv, h, kh,
                          true);
-    store_state(base, 32 * wave, r16, kg, st);
+    store_state(base, kRows * wave, r16, kg, st);
   } else {
     const int c0 = ((role - Hv) * kStepThreads + threadIdx.x) * 8;
     if (c0 >= C) return;
@@ -618,7 +657,7 @@ hipError_t launch_decode_fused(const void* x, int64_t xs, int act, const float* 
   const int G = Hv / Hk;
   const dim3 grid(nseq * Hk);
 #define GDN_FUSED_LAUNCH(TT, GG)                                                                   \
-  hipLaunchKernelGGL((fused_kernel<TT, GG>), grid, dim3(256 * GG), 0, st, static_cast<const TT*>(x), xs, w, \
+  hipLaunchKernelGGL((fused_kernel<TT, GG>), grid, dim3(kStepThreads * GG), 0, st, static_cast<const TT*>(x), xs, w, \
                      bias, conv_state, cu, Hk, Hv, eps, g, beta, state, has_init, static_cast<TT*>(o),     \
                      static_cast<TT*>(k_out), static_cast<TT*>(v_out), write_conv_state, commit_state)
   if (act == GDN_F32) {
