@@ -212,6 +212,7 @@ int gdn_decode_fused(const void* x, int64_t xs, int act, const float* w, const f
   if (!(eps > 0.f)) return fail(GDN_ERR_SHAPE, "eps must be > 0");
   const int C = 2 * Hk * dk + Hv * dv;
   if (xs < C) return fail(GDN_ERR_SHAPE, "x_row_stride must be >= C");
+  if (xs > (int64_t)(1 << 24)) return fail(GDN_ERR_SHAPE, "x_row_stride above 2^24 elements");
   if (nseq == 0 || N == 0) return GDN_OK;
   if (!x || !w || !conv_state || !cu || !g || !beta || !state || !o)
     return fail(GDN_ERR_NULL, "x, w, conv_state, cu_seqlens, g, beta, state and o are required");

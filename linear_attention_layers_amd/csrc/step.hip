@@ -64,7 +64,7 @@ template <class T> struct WaveScratch {
 
 // The block's K and Q rows, shared by the workgroup's waves (each wave
 // stages one 32-column slice), and every wave's scratch.
-template <class T> struct StepSmem {
+template <class T> struct alignas(16) StepSmem {
   using E = typename Prec<T>::E;
   static constexpr int LDK = 128 + Prec<T>::PAD;
   E K[kWin * LDK];
@@ -343,13 +343,6 @@ __device__ __forceinline__ void run_window(StepSmem<T>& sm, int wave, int lane, 
   }
 }
 
-__device__ __forceinline__ void zero_state(f32x4 (&st)[kRB][8]) {
-#pragma unroll
-  for (int b = 0; b < kRB; ++b)
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb) st[b][cb] = zero4();
-}
-
 // One workgroup per (sequence, v-head).  The state is read unconditionally
 // right after the first block's token inputs (a state without an initial
 // value is read and then discarded), so no load waits on the flag.
@@ -374,8 +367,7 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_ker
   BlockIn<T, true> in;
   load_block<T, true>(in, lane, wave, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
   f32x4 st[kRB][8];
-  load_state(base, true, v0, r16, kg, st);
-  if (!init) zero_state(st);
+  load_state(base, init, v0, r16, kg, st);   // zeros without an initial state
   run_window<T, true>(sm, wave, lane, st, in, q, k, v, g, beta, o, bos, len, Hk, Hv, h, kh,
                       commit_state != 0);
   if (commit_state) store_state(base, v0, r16, kg, st);
@@ -389,19 +381,41 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_ker
 // q and k of the k-head and v of its v-heads.  Its optional in-place
 // conv_state update therefore cannot race with another workgroup.
 //
-// Per block of up to 16 tokens: phase A computes y, rounds it to the
-// activation dtype (as the stored y would be), applies the post-conv lane
-// function (as the post-conv kernel does) and writes q, k and each v-head's
-// v, rounded again, into LDS tiles; phase B runs the step's block function
-// on fragments read from those tiles.  Every value is what the three
-// separate launches produce, so the results are bitwise equal to them.
-template <class T, int G> struct FusedSmem {
+// Per block of up to 16 tokens: the block's conv input rows (and, for the
+// first block, the stored conv rows) are staged into LDS; phase A computes
+// y from them, rounds it to the activation dtype (as the stored y would
+// be), applies the post-conv lane function (as the post-conv kernel does)
+// and writes q, k and each v-head's v, rounded again, into LDS tiles; phase
+// B runs the step's block function on fragments read from those tiles.
+// Every value is what the three separate launches produce, so the results
+// are bitwise equal to them.
+//
+// Load order.  One in-order counter covers a wave's vector memory
+// operations, so the first block's staged rows, the conv weights and the
+// gates are requested before the state: phase A then waits only for them
+// while the state is still arriving.
+template <class T, int G> struct alignas(16) FusedSmem {
   using E = typename Prec<T>::E;
   static constexpr int LDK = 128 + Prec<T>::PAD;
+  static constexpr int CH = (2 + G) * 128;                // q, k and G v heads
+  static constexpr int NT = kStepThreads * G;
+  static constexpr int PE = 16 / sizeof(E);                // elements per 16-byte piece
+  static constexpr int XP = (kWin + 3) * CH / PE;          // pieces of the conv input rows
+  static constexpr int XI = (XP + NT - 1) / NT;            // ... per thread
+  static constexpr int CP = 3 * CH / 4;                    // pieces of the stored rows
+  static constexpr int CI = (CP + NT - 1) / NT;
+  static constexpr int WI = (CH + NT - 1) / NT;            // conv taps: one piece per channel
+  static constexpr int BI = (CH / 4 + NT - 1) / NT;        // bias: four channels per piece
   WaveScratch<T> w[kStepWaves * G];
   E Qs[kWin * LDK];
   E Ks[kWin * LDK];
   E Vs[G][kWin * LDK];
+  // conv input rows, row r = block token r - 3, [kWin + 3][CH] row-major
+  // (padded to whole pieces per thread); stored rows [3][CH]
+  alignas(16) E Xs[XI * NT * PE];
+  alignas(16) float Cs[CI * NT * 4];
+  alignas(16) float Wt[4][WI * NT];    // taps, transposed: [tap][channel]
+  alignas(16) float Bt[BI * NT * 4];   // [CH] bias (zeros without one)
 };
 
 template <class T, int G>
@@ -413,8 +427,11 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
     int write_conv_state, int commit_state) {
   using PR = Prec<T>;
   using E = typename PR::E;
-  constexpr int LDK = FusedSmem<T, G>::LDK;
-  __shared__ FusedSmem<T, G> sm;
+  using SM = FusedSmem<T, G>;
+  constexpr int LDK = SM::LDK, CH = SM::CH, NT = SM::NT, PE = SM::PE;
+  constexpr int ES = sizeof(E);
+  constexpr int NW = kStepWaves * G;                      // waves
+  __shared__ SM sm;
   const int s = blockIdx.x / Hk, kh = blockIdx.x % Hk;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -427,76 +444,155 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
   if (len <= 0) return;
   const bool init = has_init == nullptr || has_init[s] != 0;
   float* cs = conv_state + (int64_t)s * 3 * C;
+  // global channel of channel c (0 .. CH-1) of this workgroup: slots 0, 1
+  // are the q and k heads of k-head kh, slots 2.. its v heads
+  auto chan = [=](int c) {
+    const int hs = c >> 7;
+    const int qk = hs * Hk + kh, vh = 2 * Hk + kh * G + hs - 2;   // both formed, one kept
+    return (hs < 2 ? qk : vh) * 128 + (c & 127);
+  };
+
+  // staged pieces: x rows of block c0 (rows before the sequence read as
+  // zeros), and the stored rows for the first block (zeros without an
+  // initial state); padding pieces read out of range (zeros)
+  u32x4 px[SM::XI], pc[SM::CI], pw[SM::WI], pb[SM::BI];
+  auto issue_stage = [&](int c0, int n) {
+    const int hb = c0 > 0 ? 3 : 0;   // rows of the previous block inside the range
+    const auto rx = buf_rsrc(x + ((int64_t)bos + c0 - hb) * xs, (n + hb) * (int)xs * ES);
+#pragma unroll
+    for (int i = 0; i < SM::XI; ++i) {
+      const int p = tid + NT * i, pp = min(p, SM::XP - 1);
+      const int row = pp / (CH / PE), c = (pp % (CH / PE)) * PE;
+      const int off = ((row - 3 + hb) * (int)xs + chan(c)) * ES;
+      px[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, p < SM::XP ? off : INT_MIN, 0, 0);
+    }
+    if (c0 == 0) {
+      const auto rc = buf_rsrc(cs, init ? 3 * C * 4 : 0);
+#pragma unroll
+      for (int i = 0; i < SM::CI; ++i) {
+        const int p = tid + NT * i, pp = min(p, SM::CP - 1);
+        const int row = pp / (CH / 4), c = (pp % (CH / 4)) * 4;
+        const int off = (row * C + chan(c)) * 4;
+        pc[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, p < SM::CP ? off : INT_MIN, 0, 0);
+      }
+      const auto rw = buf_rsrc(w, C * 16);
+#pragma unroll
+      for (int i = 0; i < SM::WI; ++i) {
+        const int p = tid + NT * i, off = chan(min(p, CH - 1)) * 16;
+        pw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, p < CH ? off : INT_MIN, 0, 0);
+      }
+      const auto rb = buf_rsrc(bias, bias != nullptr ? C * 4 : 0);
+#pragma unroll
+      for (int i = 0; i < SM::BI; ++i) {
+        const int p = tid + NT * i, off = chan(4 * min(p, CH / 4 - 1)) * 4;
+        pb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, p < CH / 4 ? off : INT_MIN, 0, 0);
+      }
+    }
+  };
+  auto write_stage = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < SM::XI; ++i) reinterpret_cast<u32x4*>(sm.Xs)[tid + NT * i] = px[i];
+    if (c0 == 0) {
+#pragma unroll
+      for (int i = 0; i < SM::CI; ++i) reinterpret_cast<u32x4*>(sm.Cs)[tid + NT * i] = pc[i];
+      // (the whole piece is reinterpreted, then indexed: a bit cast of one
+      // vector element compiled to a read of element 0 for every index)
+#pragma unroll
+      for (int i = 0; i < SM::WI; ++i) {
+        const f32x4 wv = __builtin_bit_cast(f32x4, pw[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sm.Wt[j][tid + NT * i] = wv[j];
+      }
+#pragma unroll
+      for (int i = 0; i < SM::BI; ++i) reinterpret_cast<u32x4*>(sm.Bt)[tid + NT * i] = pb[i];
+    }
+  };
+
+  // phase A lanes: 16-lane row hs = lane / 16 is one head (q, k, v...),
+  // lane jl owns its channels 8 jl .. 8 jl + 7; wave wv takes tokens
+  // wv, wv + NW, ...  Rows past the 2 + G heads idle.
+  const int hs = lane >> 4, jl = lane & 15;
+  const bool a_row = hs < 2 + G;
+
+  int n = min(kWin, len);
+  issue_stage(0, n);
+  float gl, bl;
+  auto load_gates = [&](int c0, int nn) {
+    const auto rg = buf_rsrc(g + ((int64_t)bos + c0) * Hv, nn * Hv * 4);
+    const auto rbt = buf_rsrc(beta + ((int64_t)bos + c0) * Hv, nn * Hv * 4);
+    const int goff = ((lane & 15) * Hv + h) * 4;
+    gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
+    bl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbt, goff, 0, 0));
+  };
+  load_gates(0, n);
 
   f32x4 st[kRB][8];
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
-  load_state(base, true, v0, r16, kg, st);
-  if (!init) zero_state(st);
+  load_state(base, init, v0, r16, kg, st);
+  write_stage(0);   // waits for the staged pieces only
 
-  // phase A unit = (token, head) on one 16-lane row; head 0 = q, 1 = k,
-  // 2 + j = v of v-head kh * G + j; lane j of the row owns channels 8j..8j+7
-  const int row = tid >> 4, jl = tid & 15;
-  auto channel = [&](int hd) {
-    return (hd == 0 ? kh * 128 : hd == 1 ? (Hk + kh) * 128 : (2 * Hk + kh * G + hd - 2) * 128) + 8 * jl;
-  };
   for (int c0 = 0; c0 < len; c0 += kWin) {
-    const int n = min(kWin, len - c0);
-    for (int unit = row; unit < kWin * (2 + G); unit += kStepThreads * G / 16) {
-      const int tok = unit % kWin, hd = unit / kWin;
-      const int ch = channel(hd);
-      float out[8];
-      if (tok < n) {
-        const int t = c0 + tok;   // window-relative token
-        float xe[4][8];           // xe[t-3 .. t]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tr = t - 3 + r;
-          if (tr >= 0) {
-            Act<T>::load8(x + (int64_t)(bos + tr) * xs + ch, xe[r]);
-          } else if (init) {
-            const float* p = cs + (int64_t)(3 + tr) * C + ch;
-            const float4 a = *reinterpret_cast<const float4*>(p), b4 = *reinterpret_cast<const float4*>(p + 4);
-            xe[r][0] = a.x; xe[r][1] = a.y; xe[r][2] = a.z; xe[r][3] = a.w;
-            xe[r][4] = b4.x; xe[r][5] = b4.y; xe[r][6] = b4.z; xe[r][7] = b4.w;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xe[r][i] = 0.f;
+    n = min(kWin, len - c0);
+    if (c0 > 0) {
+      issue_stage(c0, n);
+      load_gates(c0, n);
+      write_stage(c0);
+    }
+    __syncthreads();
+
+    // phase A
+    if (a_row) {
+      const int ca = hs * 128 + 8 * jl;   // channel within the workgroup
+      for (int t = wave; t < kWin; t += NW) {
+        float out[8];
+        if (t < n) {
+          // y = bias + w_0 x_{t-3} + ... + w_3 x_t, one tap at a time (the
+          // conv kernel's order): staging row t + r holds x_{t-3+r}
+          float yv[8];
+          {
+            const float4 b0 = *reinterpret_cast<const float4*>(&sm.Bt[ca]);
+            const float4 b1 = *reinterpret_cast<const float4*>(&sm.Bt[ca + 4]);
+            yv[0] = b0.x; yv[1] = b0.y; yv[2] = b0.z; yv[3] = b0.w;
+            yv[4] = b1.x; yv[5] = b1.y; yv[6] = b1.z; yv[7] = b1.w;
           }
-        }
-        float yv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 wv = *reinterpret_cast<const float4*>(w + (int64_t)(ch + i) * 4);
-          float acc = bias != nullptr ? bias[ch + i] : 0.f;
-          acc = __builtin_fmaf(wv.x, xe[0][i], acc);
-          acc = __builtin_fmaf(wv.y, xe[1][i], acc);
-          acc = __builtin_fmaf(wv.z, xe[2][i], acc);
-          acc = __builtin_fmaf(wv.w, xe[3][i], acc);
-          yv[i] = acc;
-        }
-        // y as stored in the activation dtype
-        typename Act<T>::Raw ry;
-        {
-          E tmp[8];
-          Act<T>::store8(tmp, yv);
-          ry = Act<T>::load_raw(tmp);
-        }
-        Act<T>::unpack(ry, yv);
-        postconv_lane<T>(yv, hd < 2, eps, out);
-      } else {
-        // every lane of the row takes part in the row reduction
-        float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        postconv_lane<T>(zero, false, eps, out);
+          for (int r = 0; r < 4; ++r) {
+            const int sr = t + r;
+            float xr[8];
+            if (c0 == 0 && sr < 3) {
+              const float4 a = *reinterpret_cast<const float4*>(&sm.Cs[sr * CH + ca]);
+              const float4 b4 = *reinterpret_cast<const float4*>(&sm.Cs[sr * CH + ca + 4]);
+              xr[0] = a.x; xr[1] = a.y; xr[2] = a.z; xr[3] = a.w;
+              xr[4] = b4.x; xr[5] = b4.y; xr[6] = b4.z; xr[7] = b4.w;
+            } else {
+              Act<T>::load8(&sm.Xs[sr * CH + ca], xr);
+            }
+            const float4 w0 = *reinterpret_cast<const float4*>(&sm.Wt[r][ca]);
+            const float4 w1 = *reinterpret_cast<const float4*>(&sm.Wt[r][ca + 4]);
+            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = 0.f;
-      }
-      E* dst = hd == 0 ? sm.Qs : hd == 1 ? sm.Ks : sm.Vs[hd - 2];
-      Act<T>::store8(dst + tok * LDK + 8 * jl, out);
-      // the normalised k and the v kept for a later commit's replay
-      if (tok < n) {
-        const int64_t t = (int64_t)bos + c0 + tok;
-        if (hd == 1 && k_out != nullptr) Act<T>::store8(k_out + (t * Hk + kh) * 128 + 8 * jl, out);
-        if (hd >= 2 && v_out != nullptr) Act<T>::store8(v_out + (t * Hv + kh * G + hd - 2) * 128 + 8 * jl, out);
+            for (int i = 0; i < 8; ++i) yv[i] = __builtin_fmaf(wv[i], xr[i], yv[i]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // y as stored in the activation dtype
+          typename Act<T>::Raw ry;
+          {
+            E tmp[8];
+            Act<T>::store8(tmp, yv);
+            ry = Act<T>::load_raw(tmp);
+          }
+          Act<T>::unpack(ry, yv);
+          postconv_lane<T>(yv, hs < 2, eps, out);
+          // the normalised k and the v kept for a later commit's replay
+          const int64_t tg = (int64_t)bos + c0 + t;
+          if (hs == 1 && k_out != nullptr) Act<T>::store8(k_out + (tg * Hk + kh) * 128 + 8 * jl, out);
+          if (hs >= 2 && v_out != nullptr) Act<T>::store8(v_out + (tg * Hv + kh * G + hs - 2) * 128 + 8 * jl, out);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) out[i] = 0.f;
+        }
+        E* dst = hs == 0 ? sm.Qs : hs == 1 ? sm.Ks : sm.Vs[hs - 2];
+        Act<T>::store8(dst + t * LDK + 8 * jl, out);
       }
     }
     __syncthreads();
@@ -505,17 +601,12 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
     BlockIn<T, true> in;   // K and Q are read from the tiles
     in.n = n;
     in.t0 = (int64_t)bos + c0;
+    in.gl = gl;
+    in.bl = bl;
 #pragma unroll
     for (int b = 0; b < kRB; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) in.vv[b][e] = PR::to_f32(sm.Vs[grp][(4 * kg + e) * LDK + v0 + 16 * b + r16]);
-    {
-      const auto rg = buf_rsrc(g + in.t0 * Hv, n * Hv * 4);
-      const auto rb = buf_rsrc(beta + in.t0 * Hv, n * Hv * 4);
-      const int goff = ((lane & 15) * Hv + h) * 4;
-      in.gl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, goff, 0, 0));
-      in.bl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, goff, 0, 0));
-    }
     run_block<T, true>(sm.w[wave], sm.Ks, sm.Qs, wl, lane, st, in, o, Hv, h,
                        commit_state != 0 || c0 + kWin < len);
     __syncthreads();
@@ -523,19 +614,19 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
   if (commit_state) store_state(base, v0, r16, kg, st);
 
   // conv_state <- the last 3 rows of [stored rows ; x window] for this
-  // workgroup's channels.  One 16-lane row per head reads all three final
-  // rows before writing any, so a row shifted down from a stored row is
+  // workgroup's channels.  Each lane reads all three final rows of its
+  // channels before writing any, so a row shifted down from a stored row is
   // read and written by the same lane, in program order.
-  if (write_conv_state && row < 2 + G) {
-    const int ch = channel(row);
+  if (write_conv_state && a_row && wave == 0) {
+    const int cg = chan(hs * 128 + 8 * jl);
     float v8[3][8];
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
-      const int tr = len - 3 + r;   // xe index of final row r
+      const int tr = len - 3 + r;   // token index of final row r
       if (tr >= 0) {
-        Act<T>::load8(x + (int64_t)(bos + tr) * xs + ch, v8[r]);
+        Act<T>::load8(x + (int64_t)(bos + tr) * xs + cg, v8[r]);
       } else if (init) {
-        const float* p = cs + (int64_t)(3 + tr) * C + ch;
+        const float* p = cs + (int64_t)(3 + tr) * C + cg;
         const float4 a = *reinterpret_cast<const float4*>(p), b4 = *reinterpret_cast<const float4*>(p + 4);
         v8[r][0] = a.x; v8[r][1] = a.y; v8[r][2] = a.z; v8[r][3] = a.w;
         v8[r][4] = b4.x; v8[r][5] = b4.y; v8[r][6] = b4.z; v8[r][7] = b4.w;
@@ -546,7 +637,7 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
     }
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
-      float* p = cs + (int64_t)r * C + ch;
+      float* p = cs + (int64_t)r * C + cg;
       *reinterpret_cast<float4*>(p) = make_float4(v8[r][0], v8[r][1], v8[r][2], v8[r][3]);
       *reinterpret_cast<float4*>(p + 4) = make_float4(v8[r][4], v8[r][5], v8[r][6], v8[r][7]);
     }
