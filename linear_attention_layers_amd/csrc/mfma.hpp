@@ -37,6 +37,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int by
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
+// One 8-byte LDS read kept as its own instruction.  Left alone, the
+// compiler fuses two 8-byte reads at a constant distance (here the two
+// halves of a fragment, 32 bytes apart) into ds_read2_b64, which gfx950
+// services in about 3.4x the LDS cycles of the two separate reads (13.8
+// against 2 x 2 cycles per instruction, measured with the bank-conflict
+// counter).  The offset passes through an empty asm operand, so the two
+// addresses are not known to be a constant apart.
+__device__ __forceinline__ uint2 lds_u64(const uint16_t* p, int off) {
+  asm volatile("" : "+v"(off));
+  return *reinterpret_cast<const uint2*>(p + off);
+}
+
 template <class T> struct Prec;
 
 template <> struct Prec<uint16_t> {
@@ -47,12 +59,12 @@ template <> struct Prec<uint16_t> {
   // row-major LDS matrix, fragment of rows row0.., contraction kb..
   __device__ __forceinline__ static F16 lds16(const E* p, int ld, int row, int kb, int kg) {
     F16 f;
-    f.v = *reinterpret_cast<const uint2*>(p + row * ld + kb + 4 * kg);
+    f.v = lds_u64(p, row * ld + kb + 4 * kg);
     return f;
   }
   __device__ __forceinline__ static F32 lds32(const E* p, int ld, int row, int kb, int kg) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p + row * ld + kb + 4 * kg);
-    const uint2 b = *reinterpret_cast<const uint2*>(p + row * ld + kb + 16 + 4 * kg);
+    const uint2 a = lds_u64(p, row * ld + kb + 4 * kg);
+    const uint2 b = lds_u64(p, row * ld + kb + 16 + 4 * kg);
     F32 f;
     f.v = make_uint4(a.x, a.y, b.x, b.y);
     return f;

@@ -418,20 +418,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(
 
 constexpr int kOrderMax = 64;            // batches up to this size run longest first
 
-// K and Q tiles (64 tokens x 128 features, bf16) are stored unpadded with
-// the 8-byte granules of row r XOR-permuted by sig(r) = 4 (r % 8) +
+// K and Q tiles (64 tokens x 128 features, bf16) hold their rows with the
+// 8-byte granules of row r XOR-permuted by sig(r) = 4 (r % 8) +
 // 2 ((r / 8) % 2).  A fragment read (32 lanes: 16 rows x 2 granules) and a
 // transposing read (32 lanes: 8 rows x 4 consecutive granules) then both
 // touch each of the 64 LDS banks exactly once; no plain row padding does
-// that for both patterns.  Returns the element offset of granule g of row r.
+// that for both patterns.  Each 16-row block is followed by 16 bytes of
+// padding, which shifts a block's banks uniformly (a read never spans two
+// blocks) but keeps any two blocks, and the same position in a K and a Q
+// tile, from lying a multiple of 512 bytes apart: the compiler would fuse
+// such reads into ds_read2st64_b64, which costs about 3.4x the LDS cycles
+// of the separate reads.  Returns the element offset of granule g of row r.
+constexpr int kKQTile = BT * DK + 4 * 8;   // elements per tile, with the block padding
 __device__ __forceinline__ int kq_at(int r, int g) {
-  return 4 * (32 * r + (g ^ (4 * (r & 7) + 2 * ((r >> 3) & 1))));
+  return 4 * (32 * r + (g ^ (4 * (r & 7) + 2 * ((r >> 3) & 1)))) + 8 * (r >> 4);
 }
 
 struct __attribute__((aligned(16))) SmemWS {
   static constexpr int LDT = BT + 8;   // rows of 64 tokens (bf16)
-  uint16_t K[3][BT * DK];
-  uint16_t Q[3][BT * DK];
+  uint16_t K[3][kKQTile];
+  uint16_t Q[3][kKQTile];
   uint16_t AT[2][BT * LDT];   // off-diagonal 16x16 blocks: -A; diagonal blocks: T_bb
   uint16_t P[2][BT * LDT];
   float W[3][4][BT];          // per chunk: log2-scaled G, gamma, beta, d
