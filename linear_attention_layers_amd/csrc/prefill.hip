@@ -40,6 +40,8 @@
 // rounded to bf16 only as an MFMA operand; the 16x16 diagonal inverses are
 // float32.  float32 activations: every contraction uses
 // v_mfma_f32_16x16x4_f32 on float32 operands.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         *reinterpret_cast<u32x4*>(&sm.Q[buf][e]) = pq[it];
       }
     };
-    // gate vectors: one token per lane (wave rw == 0 only)
+    // gate vectors: one token per lane (wave rw == 3 only, which forms two tile pairs, not three)
     auto load_gates = [&](int c) {
       const int64_t c0 = bos + BT * c;
       const int bytes = chunk_len(c) * Hv * 4;
@@ -570,27 +572,10 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       Wc[2 * BT + lane] = br;
       Wc[3 * BT + lane] = lane < n ? __builtin_amdgcn_exp2f(Llast - L) : 0.f;
     };
-    // tile pair (bi, bj), bi >= bj, of K/Q buffer kb with gate vectors wb:
-    // lane (r16, kg) forms rows i = 16 bi + r16, columns j = 16 bj + 4 kg + e
-    // of P and A (transposed products: K_bj-rows as the A operand)
-    auto do_pair = [&](int p, int kb, int ab, bool diag) {
-      int bi, bj;
-      tile_pair(p, bi, bj);
-      const uint16_t* Kb = sm.K[kb];
-      const uint16_t* Qb = sm.Q[kb];
-      typename PR::F32 fa[4], fq[4], fb[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        fb[t] = kq_frag(Kb, 16 * bj + r16, 32 * t, kg);
-        fq[t] = kq_frag(Qb, 16 * bi + r16, 32 * t, kg);
-        fa[t] = diag ? fb[t] : kq_frag(Kb, 16 * bi + r16, 32 * t, kg);
-      }
-      f32x4 kk = zero4(), qk = zero4();
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        kk = PR::mma32(fb[t], fa[t], kk);
-        qk = PR::mma32(fb[t], fq[t], qk);
-      }
+    // P and -A of tile pair (bi, bj), bi >= bj, from its products kk, qk:
+    // lane (r16, kg) holds rows i = 16 bi + r16, columns j = 16 bj + 4 kg + e
+    // (transposed products: K_bj-rows as the A operand)
+    auto pair_store = [&](bool diag, int bi, int bj, f32x4 kk, f32x4 qk, int kb, int ab) __attribute__((always_inline)) {
       const float* Wl = &sm.W[kb][0][0];
       const int i = 16 * bi + r16, j0 = 16 * bj + 4 * kg;
       const float Li = Wl[i], bti = Wl[2 * BT + i];
@@ -609,6 +594,47 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       else
         *reinterpret_cast<u32x2*>(&sm.AT[ab][i * LDT + j0]) =
             u32x2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
+    };
+    // this wave's tile pairs of K/Q buffer kb: (rw, rw) on the diagonal, the
+    // pair tile_pair(4 + rw) and, for rw < 2, tile_pair(8 + rw) (the ten
+    // lower pairs over four waves).  Their fragments are read one 32-wide
+    // contraction slice at a time for all pairs together, so the pairs' MFMA
+    // chains and LDS reads overlap instead of running one pair after
+    // another.  The third pair is a compile-time variant, chosen once.
+    auto pairs_t = [&](auto third_c, int kb, int ab) __attribute__((always_inline)) {
+      constexpr bool kThird = decltype(third_c)::value;
+      const uint16_t* Kb = sm.K[kb];
+      const uint16_t* Qb = sm.Q[kb];
+      const int bd = rw;                                   // diagonal block
+      const int bi1 = rw < 3 ? rw + 1 : 2, bj1 = rw < 3 ? rw : 0;
+      const int bi2 = 3, bj2 = rw == 0 ? 1 : 0;
+      f32x4 kk0 = zero4(), qk0 = zero4(), kk1 = zero4(), qk1 = zero4(), kk2 = zero4(), qk2 = zero4();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const auto d0 = kq_frag(Kb, 16 * bd + r16, 32 * t, kg);
+        const auto q0 = kq_frag(Qb, 16 * bd + r16, 32 * t, kg);
+        const auto b1 = kq_frag(Kb, 16 * bj1 + r16, 32 * t, kg);
+        const auto a1 = kq_frag(Kb, 16 * bi1 + r16, 32 * t, kg);
+        const auto q1 = kq_frag(Qb, 16 * bi1 + r16, 32 * t, kg);
+        kk0 = PR::mma32(d0, d0, kk0);
+        qk0 = PR::mma32(d0, q0, qk0);
+        kk1 = PR::mma32(b1, a1, kk1);
+        qk1 = PR::mma32(b1, q1, qk1);
+        if constexpr (kThird) {
+          const auto b2 = kq_frag(Kb, 16 * bj2 + r16, 32 * t, kg);
+          const auto a2 = kq_frag(Kb, 16 * bi2 + r16, 32 * t, kg);
+          const auto q2 = kq_frag(Qb, 16 * bi2 + r16, 32 * t, kg);
+          kk2 = PR::mma32(b2, a2, kk2);
+          qk2 = PR::mma32(b2, q2, qk2);
+        }
+      }
+      pair_store(true, bd, bd, kk0, qk0, kb, ab);
+      pair_store(false, bi1, bj1, kk1, qk1, kb, ab);
+      if constexpr (kThird) pair_store(false, bi2, bj2, kk2, qk2, kb, ab);
+    };
+    auto pairs = [&](int kb, int ab) __attribute__((always_inline)) {
+      if (rw < 2) pairs_t(std::true_type{}, kb, ab);
+      else pairs_t(std::false_type{}, kb, ab);
     };
     // T_bb = (I + A_bb)^-1 of this wave's diagonal block b = rw, by forward
     // substitution.  Lane (c, q) = (lane / 4, lane % 4) owns rows q, q+4,
@@ -639,31 +665,29 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + 16 * bb + c], x[m]);
     };
     // all factors of chunk c (K/Q and gate buffer c % 3 -> factor buffer c & 1)
-    auto factors = [&](int c) {
-      const int kb = c % 3, ab = c & 1;
-      do_pair(rw, kb, ab, true);
-      do_pair(4 + rw, kb, ab, false);
-      if (rw < 2) do_pair(8 + rw, kb, ab, false);
+    auto factors = [&](int c) __attribute__((always_inline)) {
+      const int ab = c & 1;
+      pairs(c % 3, ab);
       invert_diag(ab);
     };
 
     load_kq(0);
-    if (rw == 0) load_gates(0);
+    if (rw == 3) load_gates(0);
     stage_kq(0);
-    if (rw == 0) scan(0);
+    if (rw == 3) scan(0);
     load_kq(1);
-    if (rw == 0) load_gates(1);
+    if (rw == 3) load_gates(1);
     __syncthreads();
     factors(0);
     stage_kq(1);
-    if (rw == 0) scan(1);
+    if (rw == 3) scan(1);
     load_kq(2);
-    if (rw == 0) load_gates(2);
+    if (rw == 3) load_gates(2);
     __syncthreads();
     for (int c = 0; c < nc; ++c) {
       stage_kq((c + 2) % 3);
       load_kq(c + 3);
-      if (rw == 0) {
+      if (rw == 3) {
         scan(c + 2);
         load_gates(c + 3);
       }
