@@ -368,6 +368,10 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_ker
   load_block<T, true>(in, lane, wave, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
   f32x4 st[kRB][8];
   load_state(base, init, v0, r16, kg, st);   // zeros without an initial state
+  // every state read is issued before anything uses one: the scheduler
+  // would otherwise hoist the first block's conversions between the reads,
+  // and the in-order wait for them would hold back the remaining reads
+  __builtin_amdgcn_sched_barrier(0);
   run_window<T, true>(sm, wave, lane, st, in, q, k, v, g, beta, o, bos, len, Hk, Hv, h, kh,
                       commit_state != 0);
   if (commit_state) store_state(base, v0, r16, kg, st);
@@ -675,6 +679,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void commit_kernel(
     load_block<T, false>(in, lane, wave, nullptr, static_cast<const T*>(io.k), static_cast<const T*>(io.v), io.g,
                          io.beta, bos, min(kWin, n), Hk, Hv, h, kh, kRows * wave);
     load_state(base, init, kRows * wave, r16, kg, st);
+    __builtin_amdgcn_sched_barrier(0);   // all state reads issued before any use
     run_window<T, false>(sm, wave, lane, st, in, nullptr, static_cast<const T*>(io.k),
                          static_cast<const T*>(io.v), io.g, io.beta, nullptr, bos, n, Hk, Hv, h, kh,
                          true);
