@@ -39,16 +39,72 @@ constexpr int kConvChannelsPerBlock = 64 * kConvChannelsPerLane;   // 256
 constexpr int kConvTokensPerWave = 16;            // 4 waves x 16 = one 64-token chunk
 
 // ------------------------------------------------------------ chunk builder
-// One workgroup: sequences are scanned 256 at a time; thread i of a round
-// counts the chunks of its sequence, an exclusive scan gives each sequence
-// its first slot, and the thread writes its descriptors.  Slots past the
-// total are marked unused (seq = -1).
+// One workgroup.  Up to 64 sequences: wave 0 counts each sequence's chunks
+// (lane s), an integer prefix sum over the wave gives each its first slot,
+// and after one barrier every thread writes slots tid, tid + 256, ...,
+// finding the sequence of its slot by binary search over the first slots
+// (the last sequence whose first slot is <= the slot; empty sequences share
+// their successor's first slot and are passed over).  Larger batches are
+// scanned 256 sequences at a time.  Slots past the total are marked unused
+// (seq = -1).
+__device__ __forceinline__ int wave_prefix_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return v;
+}
+
+__device__ __forceinline__ gdn_chunk chunk_of(int s, int j, int n, int begin, int len, int chunk_len) {
+  gdn_chunk c;
+  c.seq = s;
+  c.begin = begin + j * chunk_len;
+  c.end = min(c.begin + chunk_len, begin + len);
+  c.flags = (j == 0 ? GDN_CHUNK_FIRST : 0) | (j == n - 1 ? GDN_CHUNK_LAST : 0);
+  return c;
+}
+
 __global__ __launch_bounds__(256) void make_chunks_kernel(const int32_t* __restrict__ cu, int nseq,
                                                           int chunk_len, gdn_chunk* __restrict__ out,
                                                           int cap) {
   __shared__ int s_count[256];
+  __shared__ int s_first[65];
   __shared__ int s_base;
   const int tid = threadIdx.x;
+  if (nseq <= 64) {
+    if (tid < 64) {
+      const int s = tid;
+      int n = 0;
+      if (s < nseq) {
+        const int len = cu[s + 1] - cu[s];
+        n = len > 0 ? (len + chunk_len - 1) / chunk_len : 0;
+      }
+      const int incl = wave_prefix_sum_i32(n);
+      s_first[s] = incl - n;
+      if (s == 63) s_first[64] = incl;   // the total
+    }
+    __syncthreads();
+    const int total = s_first[64];
+    for (int slot = tid; slot < cap; slot += 256) {
+      gdn_chunk c;
+      if (slot < total) {
+        int lo = 0, hi = nseq - 1;   // last s with first[s] <= slot
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_first[mid] <= slot) lo = mid; else hi = mid - 1;
+        }
+        const int begin = cu[lo], len = cu[lo + 1] - begin;
+        const int n = (len + chunk_len - 1) / chunk_len;
+        c = chunk_of(lo, slot - s_first[lo], n, begin, len, chunk_len);
+      } else {
+        c.seq = -1; c.begin = 0; c.end = 0; c.flags = 0;
+      }
+      out[slot] = c;
+    }
+    return;
+  }
   if (tid == 0) s_base = 0;
   __syncthreads();
   for (int s0 = 0; s0 < nseq; s0 += 256) {
@@ -72,14 +128,7 @@ __global__ __launch_bounds__(256) void make_chunks_kernel(const int32_t* __restr
     const int first = base + s_count[tid] - n;
     for (int j = 0; j < n; ++j) {
       const int slot = first + j;
-      if (slot < cap) {
-        gdn_chunk c;
-        c.seq = s;
-        c.begin = begin + j * chunk_len;
-        c.end = min(c.begin + chunk_len, begin + len);
-        c.flags = (j == 0 ? GDN_CHUNK_FIRST : 0) | (j == n - 1 ? GDN_CHUNK_LAST : 0);
-        out[slot] = c;
-      }
+      if (slot < cap) out[slot] = chunk_of(s, j, n, begin, len, chunk_len);
     }
     __syncthreads();
     if (tid == 255) s_base = base + s_count[255];
