@@ -346,6 +346,26 @@ def _unit_lower_inverse(A):
 # a6: commit of a speculative window
 # --------------------------------------------------------------------------
 
+def out_norm_gated(o, z, w, eps):
+    """Gated output norm after the recurrence [strata, "Summary" item 2 and
+    "Code Object Resource Usage": an output-norm kernel consumes o and a gate
+    operand z; the pages print no formula].
+
+    Reading (the plainest one the rest supports, as in the Gated DeltaNet
+    layer): per token and v-head, root-mean-square normalisation of o over
+    its dv channels, an optional per-channel weight w (ones when None), and
+    the gate SiLU(z):
+        y_i = o_i / sqrt(mean_j(o_j^2) + eps) * w_i * SiLU(z_i).
+    o, z: [..., dv]; w: [dv] or None; eps >= 0.  Returns float64."""
+    o = np.asarray(o, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    y = o / np.sqrt(ms + eps)
+    if w is not None:
+        y = y * np.asarray(w, dtype=np.float64)
+    return y * silu(z)
+
+
 def commit(x, conv_state, state, k, v, g, beta, has_init, cu_seqlens, n_keep, Hk, Hv):
     """Commit of one layer after a speculative-verify window [strata,
     "Problem and result" item 2 and "Summary" item 1: the forward ran with

@@ -525,3 +525,67 @@ def test_conv_pins_catch_reversed_taps_and_wrong_state_row_order():
     assert np.array_equal(y[0], want0)
     assert not np.array_equal(y_rev[0], want0)
     assert not np.array_equal(y_flip[0], want0)
+
+
+# ---------------------------------------------------------------------------
+# gated output norm
+# ---------------------------------------------------------------------------
+
+def _out_norm_pins_pass(fn):
+    """True when fn(o, z, w, eps) passes every output-norm pin below."""
+    r = np.random.default_rng(77)
+    dv = 128
+    o = r.standard_normal((5, 3, dv)) * 2.0
+    z = r.standard_normal((5, 3, dv)) * 3.0
+    w = r.uniform(0.5, 1.5, dv)
+    # 1. constant rows: RMS = |c|, so y = sign(c) * w * SiLU(z) with eps = 0
+    c = np.full((2, dv), -2.5)
+    zc = r.standard_normal((2, dv))
+    want = -1.0 * w * zc * scipy.special.expit(zc)
+    if not np.allclose(fn(c, zc, w, 0.0), want, rtol=1e-13, atol=0):
+        return False
+    # 2. unit RMS of y / SiLU(z) for a large gate (SiLU(40) == 40 in float64)
+    y = fn(o, np.full_like(o, 40.0), None, 0.0) / 40.0
+    if not np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13, atol=0):
+        return False
+    # 3. scale invariance with eps = 0, and a zero gate gives zero
+    if not np.allclose(fn(3.0 * o, z, w, 0.0), fn(o, z, w, 0.0), rtol=1e-12, atol=0):
+        return False
+    if np.any(fn(o, np.zeros_like(z), w, 1e-6) != 0.0):
+        return False
+    # 4. the library's RMS norm (float64 torch, CPU) times the library SiLU
+    for eps in (1e-6, 0.5):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(o), (dv,), weight=torch.from_numpy(w), eps=eps)
+        ref = (ref * torch.nn.functional.silu(torch.from_numpy(z))).numpy()
+        if not np.allclose(fn(o, z, w, eps), ref, rtol=1e-12, atol=1e-15):
+            return False
+    return True
+
+
+def test_out_norm_pins_accept_the_oracle():
+    assert _out_norm_pins_pass(O.out_norm_gated)
+
+
+def _mutant_out_norm(kind):
+    def fn(o, z, w, eps):
+        o = np.asarray(o, dtype=np.float64)
+        z = np.asarray(z, dtype=np.float64)
+        ww = np.ones(o.shape[-1]) if w is None else np.asarray(w, dtype=np.float64)
+        if kind == "sum_not_mean":
+            d = np.sqrt(np.sum(o * o, axis=-1, keepdims=True) + eps)
+        elif kind == "eps_outside":
+            d = np.sqrt(np.mean(o * o, axis=-1, keepdims=True)) + eps
+        else:
+            d = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+        y = o / d * ww
+        if kind == "sigmoid_gate":
+            return y * scipy.special.expit(z)
+        if kind == "weight_dropped":
+            return o / d * O.silu(z)
+        return y * O.silu(z)
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["sum_not_mean", "eps_outside", "sigmoid_gate", "weight_dropped"])
+def test_out_norm_pins_catch_planted_mutation(kind):
+    assert not _out_norm_pins_pass(_mutant_out_norm(kind))
