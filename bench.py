@@ -25,9 +25,11 @@ the dominant kernel's roofline, throughput in layer-tokens/s:
   verify-fused, mixed-fused
           the same, with the decode / draft tokens' conv, post-conv and
           step in one fused launch per layer
+  out-norm
+          the gated output norm on the mixed serving step's o, 24 layers
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                  [--workload varlen|verify|long|mixed|verify-fused|mixed-fused]
+                  [--workload varlen|verify|long|mixed|verify-fused|mixed-fused|out-norm]
 """
 from __future__ import annotations
 
@@ -52,6 +54,7 @@ KERNEL_SOURCES = {
     "step": ["step.hip", "mfma.hpp", "device_common.hpp"],
     "commit": ["step.hip", "mfma.hpp", "device_common.hpp"],
     "fused": ["step.hip", "mfma.hpp", "device_common.hpp"],
+    "out_norm": ["outnorm.hip", "mfma.hpp", "device_common.hpp"],
 }
 STATE_BYTES = 128 * 128 * 4   # one float32 state matrix (dv x dk)
 
@@ -350,9 +353,34 @@ def plan_mixed(dev, fused=False):
     return p
 
 
+def plan_out_norm(dev):
+    """The gated output norm on every layer's o of the mixed serving step
+    (24 layers, its token count, 16 v-heads of 128, bf16, with a weight).
+    o, z and the weight are drawn on the device (seeded)."""
+    import torch
+    from linear_attention_layers_amd import gdn, inputs
+    L = 24
+    N = sum(inputs.mixed_lengths(5000))
+    Hv = inputs.GEO_6144.Hv
+    p = Plan()
+    gen = torch.Generator(device=dev).manual_seed(6000)
+    for layer in range(L):
+        o = torch.randn(N, Hv, 128, generator=gen, device=dev).to(torch.bfloat16)
+        z = (2.0 * torch.randn(N, Hv, 128, generator=gen, device=dev)).to(torch.bfloat16)
+        w = 0.5 + torch.rand(128, generator=gen, device=dev)
+        y = torch.empty_like(o)
+        p.add("out_norm", lambda o=o, z=z, w=w, y=y: gdn.gdn_out_norm(o, z, w, 1e-6, y=y),
+              3 * N * Hv * 128 * 2 + 128 * 4)
+        p.keep.append((o, z, w, y))
+        p.tokens += N
+    p.config = {"workload": "out_norm_24L_bf16", "tokens_per_layer": N, "Hv": Hv, "head_dim": 128,
+                "layers": L, "seed": 6000}
+    return p
+
+
 PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed,
          "verify-fused": lambda dev: plan_verify(dev, fused=True),
-         "mixed-fused": lambda dev: plan_mixed(dev, fused=True)}
+         "mixed-fused": lambda dev: plan_mixed(dev, fused=True), "out-norm": plan_out_norm}
 
 
 def main():
@@ -372,7 +400,7 @@ def main():
               "multi-GPU runs are not part of this build)", file=sys.stderr)
         sys.exit(2)
     default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 10, "verify-fused": 20,
-                     "mixed-fused": 10}[args.workload]
+                     "mixed-fused": 10, "out-norm": 20}[args.workload]
     steps = args.steps if args.steps is not None else default_steps
     warmup = args.warmup if args.warmup is not None else max(2, steps // 10)
 

@@ -10,6 +10,7 @@
  *   6. layer-batched commit of a verify window   gdn_commit
  *   7. fused decode / verify: conv + post-conv + step in one launch
  *                                                gdn_decode_fused
+ *   8. gated output norm after the recurrence    gdn_out_norm
  *
  * Sources (page title, section):
  *   "perf(gdn): optimize post-conv and causal-conv kernels" (vllm.cpp pull
@@ -250,6 +251,21 @@ int gdn_decode_fused(const void* x, int64_t x_row_stride, int act,
                      const uint8_t* has_initial_state, void* o,
                      void* k_out, void* v_out,
                      int write_conv_state, int commit_state, void* stream);
+
+/* ---- 8. gated output norm ---------------------------------------------------
+ * After the recurrence, per token t and v-head h over the dv = 128 channels:
+ *   y[t][h][i] = o[t][h][i] / sqrt(mean_j o[t][h][j]^2 + eps) * w[i] * SiLU(z[t][h][i])
+ * ("Strata pull request 3226", "Summary" item 2 and "Code Object Resource
+ * Usage" name an output-norm kernel on o and a gate operand z; the pages
+ * print no formula, this is the plainest reading).  Arithmetic in float32;
+ * the sum of squares uses the post-conv kernel's neighbours-first order.
+ *   o, z (device) [N, Hv, dv] in the activation dtype act, 16-byte aligned
+ *   w    (device, optional) float32 [dv]; NULL means all ones
+ *   y    (device) [N, Hv, dv] in act; may be o itself (in place), otherwise
+ *        must not overlap o, z or w (GDN_ERR_ALIAS)
+ *   dv must be 128, eps > 0 (GDN_ERR_SHAPE); N = 0 is a no-op. */
+int gdn_out_norm(const void* o, const void* z, int act, const float* w,
+                 int N, int Hv, int dv, float eps, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -238,6 +238,24 @@ int gdn_decode_fused(const void* x, int64_t xs, int act, const float* w, const f
                   "decode_fused");
 }
 
+int gdn_out_norm(const void* o, const void* z, int act, const float* w, int N, int Hv, int dv,
+                 float eps, void* y, void* stream) {
+  if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
+  if (N < 0 || Hv < 1) return fail(GDN_ERR_SHAPE, "need N >= 0 and Hv >= 1");
+  if (dv != 128) return fail(GDN_ERR_SHAPE, "dv must be 128 (got %d)", dv);
+  if (!(eps > 0.f)) return fail(GDN_ERR_SHAPE, "eps must be > 0");
+  const size_t e = elem_bytes(act);
+  const size_t n = (size_t)N * Hv * dv * e;
+  if (n >= 0x7fffffffULL) return fail(GDN_ERR_SHAPE, "N * Hv * dv elements exceed 2 GiB");
+  if (N == 0) return GDN_OK;
+  if (!o || !z || !y) return fail(GDN_ERR_NULL, "o, z and y are required");
+  if (!aligned16(o) || !aligned16(z) || !aligned16(y) || (w && !aligned16(w)))
+    return fail(GDN_ERR_ALIGN, "o, z, y and w must be 16-byte aligned");
+  if ((y != o && overlaps(y, n, o, n)) || overlaps(y, n, z, n) || (w && overlaps(y, n, w, dv * 4)))
+    return fail(GDN_ERR_ALIAS, "y must be o itself or overlap none of o, z and w");
+  return launched(gdn::launch_out_norm(o, z, act, w, N * Hv, eps, y, as_stream(stream)), "out_norm");
+}
+
 int gdn_commit(const gdn_layer_io* layers, int L, const int32_t* cu, const int32_t* n_keep,
                const uint8_t* has_init, int nseq, int C, int Hk, int Hv, int dk, int dv, int act,
                void* stream) {

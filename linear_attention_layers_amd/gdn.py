@@ -85,10 +85,12 @@ _decode_fused = _sig("gdn_decode_fused", [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _
                                           _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                           _vp])
 
+_out_norm = _sig("gdn_out_norm", [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp])
+
 EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
             "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd",
             "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_delta_rule_step", "gdn_commit",
-            "gdn_decode_fused"]
+            "gdn_decode_fused", "gdn_out_norm"]
 
 
 class GdnError(RuntimeError):
@@ -296,6 +298,28 @@ def gdn_decode_fused(x, w, bias, conv_state, cu_seqlens, g, beta, state, Hk: int
                          int(bool(write_conv_state)),
                          int(bool(commit_state)), _stream(stream)), "gdn_decode_fused")
     return o
+
+
+# ---------------------------------------------------------------- output norm
+
+def gdn_out_norm(o: torch.Tensor, z: torch.Tensor, w: Optional[torch.Tensor] = None,
+                 eps: float = 1e-6, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = o / sqrt(mean(o^2) + eps) * w * SiLU(z) per token and v-head;
+    o, z [N, Hv, 128]; w float32 [128] or None; y may be o (in place)."""
+    _dense(o, "o")
+    _dense(z, "z")
+    _require(o.dim() == 3 and o.shape == z.shape and o.dtype == z.dtype, "o, z: [N, Hv, 128] of one dtype")
+    if w is not None:
+        _dense(w, "w")
+        _require(w.dtype == torch.float32 and w.numel() == o.shape[2], "w: float32 [dv]")
+    if y is None:
+        y = torch.empty_like(o)
+    _dense(y, "y")
+    _require(y.shape == o.shape and y.dtype == o.dtype, "y: like o")
+    N, Hv, dv = o.shape
+    _check(_out_norm(_ptr(o), _ptr(z), _code(o.dtype), _ptr(w), N, Hv, dv, float(eps), _ptr(y),
+                     _stream(stream)), "gdn_out_norm")
+    return y
 
 
 # ---------------------------------------------------------------- commit

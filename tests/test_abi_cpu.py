@@ -218,3 +218,30 @@ def test_decode_fused_validation():
     assert call(vo=FAKE + 128) == ALIAS     # v_out inside x
     assert call(N=0) == OK                 # empty: no launch
     assert call(nseq=0) == OK
+
+
+def test_out_norm_validation():
+    fn = lib.gdn_out_norm
+    fn.restype = i32
+    fn.argtypes = [vp, vp, i32, vp, i32, i32, i32, f32, vp, vp]
+    base = dict(o=FAKE, z=FAKE + (1 << 24), act=1, w=None, N=10, Hv=4, dv=128, eps=1e-6,
+                y=FAKE + (2 << 24))
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return fn(a["o"], a["z"], a["act"], a["w"], a["N"], a["Hv"], a["dv"], a["eps"], a["y"], None)
+
+    assert call(dv=64) == SHAPE
+    assert call(Hv=0) == SHAPE
+    assert call(N=-1) == SHAPE
+    assert call(eps=0.0) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(act=7) == DTYPE
+    assert call(o=None) == NULL
+    assert call(y=None) == NULL
+    assert call(z=FAKE + (1 << 24) + 8) == ALIGN
+    assert call(w=FAKE + (3 << 24) + 4) == ALIGN
+    assert call(y=FAKE + 256) == ALIAS                 # partly over o
+    assert call(y=FAKE + (1 << 24)) == ALIAS           # over z
+    assert call(w=FAKE + (2 << 24) + 512) == ALIAS     # w inside y
+    assert call(N=0) == OK                             # empty: no launch

@@ -484,3 +484,66 @@ def test_decode_fused_matches_oracle():
                                            TL.np64(lb.state), hi, cu_l, geo.Hk, geo.Hv)
     TL.check_normwise(TL.np64(o), o_ref, TL.REC_BF16, axes=(2,), what="o")
     TL.check_normwise(TL.np64(st), st_ref, TL.REC_BF16, axes=(2, 3), what="state")
+
+
+# ---------------------------------------------------------------- output norm
+
+def _out_norm_inputs(act, N, Hv, seed, with_w=True):
+    g = torch.Generator().manual_seed(seed)
+    dt = TL.ACT[act]
+    o = (torch.randn(N, Hv, 128, generator=g) * 1.7).to(dt)
+    z = (torch.randn(N, Hv, 128, generator=g) * 2.0).to(dt)
+    w = (0.5 + torch.rand(128, generator=g)) if with_w else None
+    return o, z, w
+
+
+def _out_norm_check(act, o, z, w, y, eps=1e-6):
+    ref = O.out_norm_gated(TL.np64(o), TL.np64(z), None if w is None else TL.np64(w), np.float64(np.float32(eps)))
+    got = TL.np64(y)
+    if act == "f32":
+        np.testing.assert_allclose(got, ref, rtol=2e-6, atol=1e-30)
+    else:
+        d = TL.ulp_dist_bf16(y.float().cpu().numpy(), O.round_to_bf16(ref).astype(np.float32))
+        assert d.max() <= 1, f"max bf16 ulp distance {d.max()}"
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("with_w", [True, False])
+@pytest.mark.parametrize("N,Hv", [(1, 1), (37, 3), (64, 16)])
+def test_out_norm_parity(act, with_w, N, Hv):
+    o, z, w = _out_norm_inputs(act, N, Hv, 900 + N + Hv, with_w)
+    y = gdn.gdn_out_norm(o.to(DEV), z.to(DEV), TL.dev(w), 1e-6)
+    torch.cuda.synchronize()
+    _out_norm_check(act, o, z, w, y)
+
+
+def test_out_norm_in_place_equals_out_of_place():
+    o, z, w = _out_norm_inputs("bf16", 45, 5, 950)
+    od, zd, wd = o.to(DEV), z.to(DEV), w.to(DEV)
+    y = gdn.gdn_out_norm(od, zd, wd, 1e-6)
+    o2 = od.clone()
+    r = gdn.gdn_out_norm(o2, zd, wd, 1e-6, y=o2)
+    torch.cuda.synchronize()
+    assert r.data_ptr() == o2.data_ptr()
+    assert torch.equal(y, o2)
+
+
+def test_out_norm_mixed_serving_size():
+    lb = I.mixed_serving_layer(0)
+    N, Hv = lb.N, lb.geo.Hv
+    o, z, w = _out_norm_inputs("bf16", N, Hv, 960)
+    y = gdn.gdn_out_norm(o.to(DEV), z.to(DEV), w.to(DEV), 1e-6)
+    torch.cuda.synchronize()
+    _out_norm_check("bf16", o, z, w, y)
+
+
+def test_out_norm_zero_rows_and_zero_gate():
+    o = torch.zeros(3, 2, 128, dtype=torch.bfloat16)
+    z = torch.randn(3, 2, 128).to(torch.bfloat16)
+    o[1] = torch.randn(2, 128).to(torch.bfloat16)
+    z[2] = 0
+    y = gdn.gdn_out_norm(o.to(DEV), z.to(DEV), None, 1e-6)
+    torch.cuda.synchronize()
+    yc = y.cpu()
+    assert torch.all(yc[0] == 0) and torch.all(yc[2] == 0)
+    assert torch.isfinite(yc.float()).all()
