@@ -346,6 +346,28 @@ def _unit_lower_inverse(A):
 # a6: commit of a speculative window
 # --------------------------------------------------------------------------
 
+def gates(ba, A_log, dt_bias):
+    """Gate computation before the recurrence [strata, "Root Cause & RED /
+    GREEN Verification" names the gate kernels fused_gdn_ab / gdn_ab_multi;
+    vllm155, "The one thing I changed in your tests" names their packed
+    float32 input dpacked_ba and a bf16 gate-type instantiation; the pages
+    print no formula].
+
+    Reading (the plainest one the rest supports, as in the Gated DeltaNet
+    layer): the projection gives, per token and v-head, the pair (b, a)
+    packed as ba[..., h, 0] = b, ba[..., h, 1] = a; per v-head parameters
+    A_log and dt_bias; then
+        beta = sigmoid(b),   g = log a_t = -exp(A_log) * softplus(a + dt_bias).
+    ba: [N, Hv, 2]; A_log, dt_bias: [Hv].  Returns (g, beta) float64 [N, Hv]."""
+    ba = np.asarray(ba, dtype=np.float64)
+    b, a = ba[..., 0], ba[..., 1]
+    A_log = np.asarray(A_log, dtype=np.float64)
+    dt_bias = np.asarray(dt_bias, dtype=np.float64)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    g = -np.exp(A_log) * np.logaddexp(0.0, a + dt_bias)
+    return g, beta
+
+
 def out_norm_gated(o, z, w, eps):
     """Gated output norm after the recurrence [strata, "Summary" item 2 and
     "Code Object Resource Usage": an output-norm kernel consumes o and a gate

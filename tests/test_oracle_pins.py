@@ -589,3 +589,62 @@ def _mutant_out_norm(kind):
 @pytest.mark.parametrize("kind", ["sum_not_mean", "eps_outside", "sigmoid_gate", "weight_dropped"])
 def test_out_norm_pins_catch_planted_mutation(kind):
     assert not _out_norm_pins_pass(_mutant_out_norm(kind))
+
+
+# ---------------------------------------------------------------------------
+# gate computation
+# ---------------------------------------------------------------------------
+
+def _gates_pins_pass(fn):
+    """True when fn(ba, A_log, dt_bias) -> (g, beta) passes every gate pin."""
+    r = np.random.default_rng(88)
+    Hv = 6
+    # 1. closed forms: b = 0 gives beta = 1/2; a = -dt_bias gives softplus(0) = ln 2
+    A_log = r.uniform(-1.0, 1.0, Hv)
+    dt = r.uniform(-2.0, 2.0, Hv)
+    ba = np.zeros((3, Hv, 2))
+    ba[..., 1] = -dt
+    g, beta = fn(ba, A_log, dt)
+    if not np.allclose(beta, 0.5, rtol=0, atol=1e-15):
+        return False
+    if not np.allclose(g, -np.exp(A_log) * math.log(2.0), rtol=1e-14, atol=0):
+        return False
+    # 2. library special cases: beta is scipy's expit of b; with A_log = 0 and
+    #    no bias the decay is -log1p(exp(a)) (numpy)
+    ba = r.standard_normal((7, Hv, 2)) * 4.0
+    g, beta = fn(ba, np.zeros(Hv), np.zeros(Hv))
+    if not np.allclose(beta, scipy.special.expit(ba[..., 0]), rtol=1e-14, atol=0):
+        return False
+    if not np.allclose(g, -np.log1p(np.exp(ba[..., 1])), rtol=1e-13, atol=0):
+        return False
+    # 3. the decay is a log, never positive; A_log scales it by e^A_log
+    g1, _ = fn(ba, np.full(Hv, 0.7), dt)
+    g0, _ = fn(ba, np.zeros(Hv), dt)
+    if np.any(g1 > 0) or not np.allclose(g1, math.exp(0.7) * g0, rtol=1e-13, atol=0):
+        return False
+    # 4. the packing: swapping the pair changes the result (b first, a second)
+    g2, beta2 = fn(ba[..., ::-1], np.zeros(Hv), np.zeros(Hv))
+    return not np.allclose(beta2, beta)
+
+
+def test_gates_pins_accept_the_oracle():
+    assert _gates_pins_pass(O.gates)
+
+
+def _mutant_gates(kind):
+    def fn(ba, A_log, dt_bias):
+        ba = np.asarray(ba, dtype=np.float64)
+        b, a = (ba[..., 1], ba[..., 0]) if kind == "swapped_pair" else (ba[..., 0], ba[..., 1])
+        beta = 1.0 / (1.0 + np.exp(-b))
+        scale = np.asarray(A_log) if kind == "A_log_not_exponentiated" else np.exp(A_log)
+        x = a if kind == "bias_dropped" else a + np.asarray(dt_bias)
+        g = -scale * np.logaddexp(0.0, x)
+        if kind == "sign":
+            g = -g
+        return g, beta
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["swapped_pair", "A_log_not_exponentiated", "bias_dropped", "sign"])
+def test_gates_pins_catch_planted_mutation(kind):
+    assert not _gates_pins_pass(_mutant_gates(kind))
