@@ -27,9 +27,10 @@ the dominant kernel's roofline, throughput in layer-tokens/s:
           step in one fused launch per layer
   out-norm
           the gated output norm on the mixed serving step's o, 24 layers
+  gates   the gate computation for the mixed serving step, 24 layers
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                  [--workload varlen|verify|long|mixed|verify-fused|mixed-fused|out-norm]
+                  [--workload varlen|verify|long|mixed|verify-fused|mixed-fused|out-norm|gates]
 """
 from __future__ import annotations
 
@@ -55,6 +56,7 @@ KERNEL_SOURCES = {
     "commit": ["step.hip", "mfma.hpp", "device_common.hpp"],
     "fused": ["step.hip", "mfma.hpp", "device_common.hpp"],
     "out_norm": ["outnorm.hip", "mfma.hpp", "device_common.hpp"],
+    "gates": ["gates.hip", "mfma.hpp", "device_common.hpp"],
 }
 STATE_BYTES = 128 * 128 * 4   # one float32 state matrix (dv x dk)
 
@@ -172,6 +174,7 @@ class Plan:
         self.count = {}          # kernel name -> launches per step
         self.flops = {}          # kernel name -> dense flops per step
         self.tokens = 0
+        self.dtype = "bf16"      # arithmetic type of the step's activations
         self.config = {}
         self.keep = []           # tensors kept alive
 
@@ -378,9 +381,36 @@ def plan_out_norm(dev):
     return p
 
 
+def plan_gates(dev):
+    """The gate computation for every layer of the mixed serving step (24
+    layers, its token count, 16 v-heads): packed float32 (b, a) in, float32
+    g and beta out.  Inputs drawn on the device (seeded)."""
+    import torch
+    from linear_attention_layers_amd import gdn, inputs
+    L = 24
+    N = sum(inputs.mixed_lengths(5000))
+    Hv = inputs.GEO_6144.Hv
+    p = Plan()
+    gen = torch.Generator(device=dev).manual_seed(7000)
+    for layer in range(L):
+        ba = 2.0 * torch.randn(N, Hv, 2, generator=gen, device=dev)
+        A_log = torch.log(1.0 + 15.0 * torch.rand(Hv, generator=gen, device=dev))
+        dt = torch.randn(Hv, generator=gen, device=dev)
+        g = torch.empty(N, Hv, device=dev)
+        beta = torch.empty_like(g)
+        p.add("gates", lambda ba=ba, A_log=A_log, dt=dt, g=g, beta=beta: gdn.gdn_gates(ba, A_log, dt, g=g, beta=beta),
+              N * Hv * 16 + Hv * 8)
+        p.keep.append((ba, A_log, dt, g, beta))
+        p.tokens += N
+    p.config = {"workload": "gates_24L_f32", "tokens_per_layer": N, "Hv": Hv, "layers": L, "seed": 7000}
+    p.dtype = "f32"
+    return p
+
+
 PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed,
          "verify-fused": lambda dev: plan_verify(dev, fused=True),
-         "mixed-fused": lambda dev: plan_mixed(dev, fused=True), "out-norm": plan_out_norm}
+         "mixed-fused": lambda dev: plan_mixed(dev, fused=True), "out-norm": plan_out_norm,
+         "gates": plan_gates}
 
 
 def main():
@@ -400,7 +430,7 @@ def main():
               "multi-GPU runs are not part of this build)", file=sys.stderr)
         sys.exit(2)
     default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 10, "verify-fused": 20,
-                     "mixed-fused": 10, "out-norm": 20}[args.workload]
+                     "mixed-fused": 10, "out-norm": 20, "gates": 20}[args.workload]
     steps = args.steps if args.steps is not None else default_steps
     warmup = args.warmup if args.warmup is not None else max(2, steps // 10)
 
@@ -491,7 +521,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": plan.dtype,
         "data": "synthetic",
         "config": plan.config,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),

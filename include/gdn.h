@@ -11,6 +11,7 @@
  *   7. fused decode / verify: conv + post-conv + step in one launch
  *                                                gdn_decode_fused
  *   8. gated output norm after the recurrence    gdn_out_norm
+ *   9. gate computation before the recurrence   gdn_gates
  *
  * Sources (page title, section):
  *   "perf(gdn): optimize post-conv and causal-conv kernels" (vllm.cpp pull
@@ -266,6 +267,24 @@ int gdn_decode_fused(const void* x, int64_t x_row_stride, int act,
  *   dv must be 128, eps > 0 (GDN_ERR_SHAPE); N = 0 is a no-op. */
 int gdn_out_norm(const void* o, const void* z, int act, const float* w,
                  int N, int Hv, int dv, float eps, void* y, void* stream);
+
+/* ---- 9. gate computation ----------------------------------------------------
+ * Before the recurrence, per token t and v-head h, from the packed pair
+ * ba[t][h] = (b, a) and the per-head parameters A_log, dt_bias:
+ *   beta[t][h] = sigmoid(b),  g[t][h] = log a_t = -exp(A_log[h]) * softplus(a + dt_bias[h])
+ * ("Strata pull request 3226", "Root Cause & RED / GREEN Verification",
+ * names the gate kernels; "perf(gdn): optimize post-conv and causal-conv
+ * kernels", "The one thing I changed in your tests", their packed float32
+ * input and a bf16 gate type; the pages print no formula, this is the
+ * plainest reading).  g and beta are the float32 gates the recurrence
+ * entry points take.  Float32 arithmetic with the HIP math library.
+ *   ba      (device) [N, Hv, 2] in gate_act (GDN_F32: 8-byte aligned,
+ *           GDN_BF16: 4-byte aligned)
+ *   A_log, dt_bias (device) float32 [Hv]
+ *   g, beta (device) float32 [N, Hv], 4-byte aligned, overlapping nothing
+ *   N = 0 is a no-op; Hv >= 1. */
+int gdn_gates(const void* ba, int gate_act, const float* A_log, const float* dt_bias,
+              int N, int Hv, float* g, float* beta, void* stream);
 
 #ifdef __cplusplus
 }

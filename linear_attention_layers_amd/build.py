@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["conv.hip", "postconv.hip", "step.hip", "prefill.hip", "outnorm.hip", "api.cpp"]
+SOURCES = ["conv.hip", "postconv.hip", "step.hip", "prefill.hip", "outnorm.hip", "gates.hip", "api.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

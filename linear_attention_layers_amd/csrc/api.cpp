@@ -238,6 +238,29 @@ int gdn_decode_fused(const void* x, int64_t xs, int act, const float* w, const f
                   "decode_fused");
 }
 
+int gdn_gates(const void* ba, int gate_act, const float* A_log, const float* dt_bias, int N, int Hv,
+              float* g, float* beta, void* stream) {
+  if (!valid_dtype(gate_act)) return fail(GDN_ERR_DTYPE, "unsupported gate dtype %d", gate_act);
+  if (N < 0 || Hv < 1) return fail(GDN_ERR_SHAPE, "need N >= 0 and Hv >= 1");
+  const size_t rows = (size_t)N * Hv;
+  if (rows * 8 >= 0x7fffffffULL) return fail(GDN_ERR_SHAPE, "N * Hv too large");
+  if (N == 0) return GDN_OK;
+  if (!ba || !A_log || !dt_bias || !g || !beta)
+    return fail(GDN_ERR_NULL, "ba, A_log, dt_bias, g and beta are required");
+  const size_t pair = gate_act == GDN_F32 ? 8 : 4;
+  if (reinterpret_cast<uintptr_t>(ba) % pair != 0 || reinterpret_cast<uintptr_t>(g) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(beta) % 4 != 0 || reinterpret_cast<uintptr_t>(A_log) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(dt_bias) % 4 != 0)
+    return fail(GDN_ERR_ALIGN, "ba must be aligned to its (b, a) pair, the float32 arrays to 4 bytes");
+  const size_t nb = rows * pair, ng = rows * 4, np = (size_t)Hv * 4;
+  if (overlaps(g, ng, beta, ng) || overlaps(g, ng, ba, nb) || overlaps(beta, ng, ba, nb) ||
+      overlaps(g, ng, A_log, np) || overlaps(g, ng, dt_bias, np) || overlaps(beta, ng, A_log, np) ||
+      overlaps(beta, ng, dt_bias, np))
+    return fail(GDN_ERR_ALIAS, "g and beta must not overlap each other or the inputs");
+  return launched(gdn::launch_gates(ba, gate_act, A_log, dt_bias, (int)rows, Hv, g, beta, as_stream(stream)),
+                  "gates");
+}
+
 int gdn_out_norm(const void* o, const void* z, int act, const float* w, int N, int Hv, int dv,
                  float eps, void* y, void* stream) {
   if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);

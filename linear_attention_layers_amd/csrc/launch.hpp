@@ -18,6 +18,8 @@ hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const
                        const gdn_chunk* chunks, int nchunks, int C, int write_state, void* y,
                        hipStream_t st);
 
+hipError_t launch_gates(const void* ba, int gate_act, const float* A_log, const float* dt_bias, int rows,
+                        int Hv, float* g, float* beta, hipStream_t st);
 hipError_t launch_out_norm(const void* o, const void* z, int act, const float* w, int rows, float eps,
                            void* y, hipStream_t st);
 hipError_t launch_postconv(const void* y, int64_t ys, int in, int N, int Hk, int Hv, float eps,

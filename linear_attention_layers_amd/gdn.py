@@ -86,11 +86,12 @@ _decode_fused = _sig("gdn_decode_fused", [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _
                                           _vp])
 
 _out_norm = _sig("gdn_out_norm", [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _vp, _vp])
+_gates = _sig("gdn_gates", [_vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp])
 
 EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
             "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd",
             "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_delta_rule_step", "gdn_commit",
-            "gdn_decode_fused", "gdn_out_norm"]
+            "gdn_decode_fused", "gdn_out_norm", "gdn_gates"]
 
 
 class GdnError(RuntimeError):
@@ -298,6 +299,31 @@ def gdn_decode_fused(x, w, bias, conv_state, cu_seqlens, g, beta, state, Hk: int
                          int(bool(write_conv_state)),
                          int(bool(commit_state)), _stream(stream)), "gdn_decode_fused")
     return o
+
+
+# ---------------------------------------------------------------- gates
+
+def gdn_gates(ba: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+              g: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None, stream=None):
+    """beta = sigmoid(b), g = -exp(A_log) * softplus(a + dt_bias) from the
+    packed ba [N, Hv, 2] = (b, a) (float32 or bf16); returns float32 (g, beta)
+    of shape [N, Hv]."""
+    _dense(ba, "ba")
+    _require(ba.dim() == 3 and ba.shape[2] == 2, "ba: [N, Hv, 2]")
+    N, Hv, _ = ba.shape
+    for t, nm in ((A_log, "A_log"), (dt_bias, "dt_bias")):
+        _dense(t, nm)
+        _require(t.dtype == torch.float32 and t.numel() == Hv, f"{nm}: float32 [Hv]")
+    if g is None:
+        g = torch.empty(N, Hv, dtype=torch.float32, device=ba.device)
+    if beta is None:
+        beta = torch.empty(N, Hv, dtype=torch.float32, device=ba.device)
+    for t, nm in ((g, "g"), (beta, "beta")):
+        _dense(t, nm)
+        _require(t.dtype == torch.float32 and t.numel() == N * Hv, f"{nm}: float32 [N, Hv]")
+    _check(_gates(_ptr(ba), _code(ba.dtype), _ptr(A_log), _ptr(dt_bias), N, Hv, _ptr(g), _ptr(beta),
+                  _stream(stream)), "gdn_gates")
+    return g, beta
 
 
 # ---------------------------------------------------------------- output norm

@@ -245,3 +245,26 @@ def test_out_norm_validation():
     assert call(y=FAKE + (1 << 24)) == ALIAS           # over z
     assert call(w=FAKE + (2 << 24) + 512) == ALIAS     # w inside y
     assert call(N=0) == OK                             # empty: no launch
+
+
+def test_gates_validation():
+    fn = lib.gdn_gates
+    fn.restype = i32
+    fn.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, vp]
+    base = dict(ba=FAKE, act=0, A=FAKE + (1 << 24), dt=FAKE + (2 << 24), N=10, Hv=4,
+                g=FAKE + (3 << 24), beta=FAKE + (4 << 24))
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return fn(a["ba"], a["act"], a["A"], a["dt"], a["N"], a["Hv"], a["g"], a["beta"], None)
+
+    assert call(Hv=0) == SHAPE
+    assert call(N=-3) == SHAPE
+    assert call(act=5) == DTYPE
+    assert call(ba=None) == NULL
+    assert call(beta=None) == NULL
+    assert call(ba=FAKE + 4) == ALIGN                    # f32 pairs need 8 bytes
+    assert call(g=FAKE + (3 << 24) + 2) == ALIGN
+    assert call(beta=FAKE + (3 << 24) + 16) == ALIAS     # overlaps g
+    assert call(g=FAKE + 40) == ALIAS                    # inside ba
+    assert call(N=0) == OK

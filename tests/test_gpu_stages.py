@@ -547,3 +547,39 @@ def test_out_norm_zero_rows_and_zero_gate():
     yc = y.cpu()
     assert torch.all(yc[0] == 0) and torch.all(yc[2] == 0)
     assert torch.isfinite(yc.float()).all()
+
+
+# ---------------------------------------------------------------- gates
+
+def _gates_inputs(act, N, Hv, seed, scale=2.0):
+    g = torch.Generator().manual_seed(seed)
+    ba = (torch.randn(N, Hv, 2, generator=g) * scale).to(TL.ACT[act])
+    A_log = torch.log(1.0 + 15.0 * torch.rand(Hv, generator=g))
+    dt = torch.randn(Hv, generator=g)
+    return ba, A_log, dt
+
+
+def _gates_check(ba, A_log, dt, g, beta):
+    g_ref, b_ref = O.gates(TL.np64(ba), TL.np64(A_log), TL.np64(dt))
+    np.testing.assert_allclose(TL.np64(g), g_ref, rtol=4e-6, atol=1e-30)
+    np.testing.assert_allclose(TL.np64(beta), b_ref, rtol=4e-6, atol=1e-30)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("N,Hv", [(1, 1), (37, 3), (5252, 32)])
+def test_gates_parity(act, N, Hv):
+    ba, A_log, dt = _gates_inputs(act, N, Hv, 970 + N + Hv)
+    g, beta = gdn.gdn_gates(ba.to(DEV), A_log.to(DEV), dt.to(DEV))
+    torch.cuda.synchronize()
+    _gates_check(ba, A_log, dt, g, beta)
+
+
+def test_gates_extreme_inputs():
+    ba = torch.tensor([[[30.0, 30.0], [-30.0, -30.0], [0.0, 19.5], [0.0, 20.5], [88.0, -88.0], [-88.0, 100.0]]])
+    A_log = torch.zeros(6)
+    dt = torch.zeros(6)
+    g, beta = gdn.gdn_gates(ba.to(DEV), A_log.to(DEV), dt.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(g).all() and torch.isfinite(beta).all()
+    assert (g <= 0).all() and (beta >= 0).all() and (beta <= 1).all()
+    _gates_check(ba, A_log, dt, g, beta)
