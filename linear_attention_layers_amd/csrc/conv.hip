@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(
   float h0[4], h1[4], h2[4];
   float* st = conv_state + ((int64_t)s * 3) * C + c0;
   if (owner) {
-    const bool init = has_init == nullptr || has_init[s] != 0;
+    const bool init = seq_flag(has_init, s);
     const float4 a = init ? *reinterpret_cast<const float4*>(st) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 bb = init ? *reinterpret_cast<const float4*>(st + C) : make_float4(0.f, 0.f, 0.f, 0.f);
     const float4 c = init ? *reinterpret_cast<const float4*>(st + 2 * C) : make_float4(0.f, 0.f, 0.f, 0.f);

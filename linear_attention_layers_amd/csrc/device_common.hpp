@@ -95,6 +95,20 @@ template <> struct Act<uint16_t> {
   }
 };
 
+// ------------------------------------------------------ per-sequence flag
+// Byte s of a per-sequence uint8 array (NULL = every flag set).  The aligned
+// dword that holds the byte is read instead of the byte: at a uniform
+// address that is a scalar load, which arrives with the prologue's other
+// scalar loads rather than as a vector load that everything after it on the
+// in-order vector counter would wait behind.  A 4-byte-aligned dword never
+// crosses a page, so reading the bytes beside the flag cannot fault.
+__device__ __forceinline__ bool seq_flag(const uint8_t* __restrict__ f, int s) {
+  if (f == nullptr) return true;
+  const int sub = static_cast<int>((reinterpret_cast<uintptr_t>(f) + static_cast<uintptr_t>(s)) & 3);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(f + s - sub);
+  return ((w >> (8 * sub)) & 0xffu) != 0;
+}
+
 // ------------------------------------------------------- wave64 DPP moves
 // Row-local (16-lane) data movement.  quad_perm xor-1 = 0xB1, xor-2 = 0x4E,
 // row_half_mirror = 0x141 (lane i <- 7-i within 8), row_mirror = 0x140

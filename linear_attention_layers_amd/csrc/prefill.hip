@@ -107,6 +107,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(
   const int s = u / Hv;
   const int kh = h / (Hv / Hk);
   const int bos = cu[s], eos = cu[s + 1];
+  const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
   int v0[VB];                               // this wave's state rows: v0[b] .. v0[b] + 15
 #pragma unroll
   for (int b = 0; b < VB; ++b) v0[b] = slice * DVS + 16 * (wave * VB + b);
@@ -114,7 +115,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(
   // ---- S^T tiles: st[b][cb][e] = S[v0[b] + r16][16 cb + 4 kg + e]
   f32x4 st[VB][8];
   float* const sbase = state + ((int64_t)s * Hv + h) * (DK * DK);
-  const bool init = has_init == nullptr || has_init[s] != 0;
 #pragma unroll
   for (int b = 0; b < VB; ++b)
 #pragma unroll
@@ -520,6 +520,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
   const int h = item / NSL;
   const int kh = h / (Hv / Hk);
   const int bos = cu[s], eos = cu[s + 1];
+  const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
   const int nc = eos > bos ? (eos - bos + BT - 1) / BT : 0;
   // valid tokens of chunk c (0 past the end)
   auto chunk_len = [&](int c) { return max(0, min(BT, eos - (bos + BT * c))); };
@@ -705,7 +706,6 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
 
   f32x4 st[VB][8];
   float* const sbase = state + ((int64_t)s * Hv + h) * (DK * DK);
-  const bool init = has_init == nullptr || has_init[s] != 0;
 #pragma unroll
   for (int b = 0; b < VB; ++b)
 #pragma unroll

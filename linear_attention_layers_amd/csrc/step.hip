@@ -343,9 +343,10 @@ __device__ __forceinline__ void run_window(StepSmem<T>& sm, int wave, int lane, 
   }
 }
 
-// One workgroup per (sequence, v-head).  The state is read unconditionally
-// right after the first block's token inputs (a state without an initial
-// value is read and then discarded), so no load waits on the flag.
+// One workgroup per (sequence, v-head).  The state is read right after the
+// first block's token inputs; without an initial state the reads go through
+// an empty buffer range and return zeros.  The flag comes from a scalar load
+// issued with cu's, so no vector load waits on it.
 template <class T>
 __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -361,9 +362,9 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_ker
   const int r16 = lane & 15, kg = lane >> 4;
   const int v0 = kRows * wave;
   const int bos = cu[s], len = cu[s + 1] - bos;
+  const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
   if (len <= 0) return;
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
-  const bool init = has_init == nullptr || has_init[s] != 0;
   BlockIn<T, true> in;
   load_block<T, true>(in, lane, wave, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
   f32x4 st[kRB][8];
@@ -445,8 +446,8 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
   const int h = kh * G + grp;
   const int C = (2 * Hk + Hv) * 128;
   const int bos = cu[s], len = cu[s + 1] - bos;
+  const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
   if (len <= 0) return;
-  const bool init = has_init == nullptr || has_init[s] != 0;
   float* cs = conv_state + (int64_t)s * 3 * C;
   // global channel of channel c (0 .. CH-1) of this workgroup: slots 0, 1
   // are the q and k heads of k-head kh, slots 2.. its v heads
@@ -663,10 +664,10 @@ __global__ __launch_bounds__(kStepThreads, 1) void commit_kernel(
   const int s = (b / roles) % nseq;
   const int layer = b / (roles * nseq);
   const int n = n_keep[s];
+  const int bos = cu[s];
+  const bool init = seq_flag(has_init, s);   // the three scalar reads overlap
   if (n <= 0) return;
   const gdn_layer_io io = layers[layer];
-  const int bos = cu[s];
-  const bool init = has_init == nullptr || has_init[s] != 0;
   if (role < Hv) {
     const int h = role;
     const int kh = h / (Hv / Hk);
