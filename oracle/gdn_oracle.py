@@ -332,6 +332,95 @@ def delta_rule_chunked(q, k, v, g, beta, state0, has_init, cu_seqlens, Hk, Hv,
     return o, st
 
 
+def segment_bounds(cu_seqlens, nseg: int, chunk_len: int = 64) -> np.ndarray:
+    """Split of every sequence into nseg segments of whole chunks, for the
+    segment-parallel evaluation below.  The pages print no such split
+    (reading): with n tokens, nc = ceil(n / chunk_len) chunks and per =
+    ceil(nc / nseg) chunks per segment, segment p covers tokens
+    [bos + min(n, p per chunk_len), bos + min(n, (p + 1) per chunk_len)), so
+    the last segments may be short or empty.  Returns int64 [nseq, nseg, 2]
+    (begin, end)."""
+    cu = [int(c) for c in cu_seqlens]
+    out = np.zeros((len(cu) - 1, nseg, 2), dtype=np.int64)
+    for s in range(len(cu) - 1):
+        n = cu[s + 1] - cu[s]
+        per = -(-(-(-n // chunk_len)) // nseg)
+        for p in range(nseg):
+            out[s, p, 0] = cu[s] + min(n, p * per * chunk_len)
+            out[s, p, 1] = cu[s] + min(n, (p + 1) * per * chunk_len)
+    return out
+
+
+def segment_transition(k, g, beta, cu_seqlens, Hk, Hv):
+    """State transition of the gated delta rule over each sequence [GDN].
+    Every token's step is affine in the state:
+        S_t = S_{t-1} M_t + b_t v_t k_t^T,   M_t = a_t (I - b_t k_t k_t^T),
+    so a run of tokens t_1 .. t_n entering with any S ends at
+        S P + R,   P = M_{t_1} M_{t_2} ... M_{t_n}   (dk x dk),
+    where R is the state the run reaches from S = 0 (delta_rule_recurrent
+    with no initial state).  P depends on k, g and beta only, not on v.  The
+    pages print no segment-parallel form (reading: this is the composition
+    of the per-token rule).  P is formed token by token, P <- P M_t, from
+    P = I.  Returns P [nseq, Hv, dk, dk], float64."""
+    k = np.asarray(k, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    kmap = _kv_head_map(Hk, Hv)
+    cu = [int(c) for c in cu_seqlens]
+    dk = k.shape[-1]
+    out = np.zeros((len(cu) - 1, Hv, dk, dk))
+    for s in range(len(cu) - 1):
+        P = np.broadcast_to(np.eye(dk), (Hv, dk, dk)).copy()
+        for t in range(cu[s], cu[s + 1]):
+            kt = k[t, kmap]                                          # [Hv, dk]
+            M = np.eye(dk)[None] - beta[t][:, None, None] * kt[:, :, None] * kt[:, None, :]
+            P = np.exp(g[t])[:, None, None] * (P @ M)
+        out[s] = P
+    return out
+
+
+def delta_rule_segmented(q, k, v, g, beta, state0, has_init, cu_seqlens, Hk, Hv, nseg,
+                         chunk_len=64):
+    """The gated delta rule evaluated segment-parallel [GDN; reading, as
+    segment_transition]: each sequence is split by segment_bounds, then
+      1. segment 0 runs from the entering state (or 0) and gives X_1, the
+         state entering segment 1; every later segment p gives its
+         transition (P_p, R_p), independently of the others;
+      2. X_{p+1} = X_p P_p + R_p for p = 1 .. nseg - 2;
+      3. every segment p >= 1 runs again from X_p, which gives its outputs
+         and, for the last segment, the final state.
+    Returns the same as delta_rule_recurrent, to which it is equal up to
+    rounding.  chunk_len is the split granularity of segment_bounds."""
+    cu = [int(c) for c in cu_seqlens]
+    bounds = segment_bounds(cu, nseg, chunk_len)
+    st0 = np.asarray(state0, dtype=np.float64)
+    N = np.asarray(q).shape[0]
+    dv = np.asarray(v).shape[-1]
+    o = np.zeros((N, Hv, dv))
+    final = np.array(st0, copy=True)
+    for s in range(len(cu) - 1):
+        def run(p, S, init):
+            b, e = int(bounds[s, p, 0]), int(bounds[s, p, 1])
+            oo, ss = delta_rule_recurrent(q, k, v, g, beta, S[None], [init], [b, e], Hk, Hv)
+            return oo[b:e], ss[0], (b, e)
+        oo, X, (b, e) = run(0, st0[s], bool(has_init[s]))
+        o[b:e] = oo
+        Ps, Rs = [None] * nseg, [None] * nseg
+        for p in range(1, nseg):
+            b, e = int(bounds[s, p, 0]), int(bounds[s, p, 1])
+            Ps[p] = segment_transition(k, g, beta, [b, e], Hk, Hv)[0]
+            Rs[p] = run(p, np.zeros_like(st0[s]), False)[1]
+        Xs = [None, X]
+        for p in range(1, nseg - 1):
+            Xs.append(Xs[p] @ Ps[p] + Rs[p])
+        for p in range(1, nseg):
+            oo, S, (b, e) = run(p, Xs[p], True)
+            o[b:e] = oo
+            X = S
+        final[s] = X
+    return o, final
+
+
 def _unit_lower_inverse(A):
     """(I + A)^-1 for strictly lower triangular A, by forward substitution:
     row i of T is e_i - sum_{j<i} A_ij T_j."""

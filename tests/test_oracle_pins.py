@@ -648,3 +648,127 @@ def _mutant_gates(kind):
 @pytest.mark.parametrize("kind", ["swapped_pair", "A_log_not_exponentiated", "bias_dropped", "sign"])
 def test_gates_pins_catch_planted_mutation(kind):
     assert not _gates_pins_pass(_mutant_gates(kind))
+
+
+# --------------------------------------------------------------------------
+# Segment transition and the segment-parallel form [GDN: the per-token rule is
+# affine in the state]
+
+def _seg_inputs(seed, N=26, Hk=2, Hv=4, d=6):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((N, Hk, d))
+    k = r.standard_normal((N, Hk, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((N, Hv, d))
+    g = -r.uniform(0.01, 0.6, (N, Hv))
+    b = r.uniform(0.05, 1.0, (N, Hv))
+    return q, k, v, g, b
+
+
+def _transition_pins_pass(fn):
+    """True when fn(k, g, beta, cu, Hk, Hv) -> P [nseq, Hv, dk, dk] passes
+    every transition pin."""
+    Hk, Hv, d = 2, 4, 6
+    q, k, v, g, b = _seg_inputs(90, Hk=Hk, Hv=Hv, d=d)
+    cu = [0, 9, 9, 26]                                  # a middle sequence is empty
+    P = fn(k, g, b, cu, Hk, Hv)
+    # 1. defining property, against the per-token recurrence (pinned by its
+    #    own tests): from any entering state S the end state is S P + R
+    r = np.random.default_rng(91)
+    S = r.standard_normal((3, Hv, d, d))
+    _, end = O.delta_rule_recurrent(q, k, v, g, b, S, [1, 1, 1], cu, Hk, Hv)
+    _, R = O.delta_rule_recurrent(q, k, v, g, b, S, [0, 0, 0], cu, Hk, Hv)
+    if not np.allclose(S @ P + R, end, rtol=1e-12, atol=1e-12):
+        return False
+    # 2. an empty run leaves the state alone: P = I
+    if not np.allclose(P[1], np.eye(d)[None], rtol=0, atol=0):
+        return False
+    # 3. one token, closed form: P = a (I - b k k^T) with the v-head's k-head
+    P1 = fn(k, g, b, [4, 5], Hk, Hv)[0]
+    kmap = np.arange(Hv) // (Hv // Hk)
+    for h in range(Hv):
+        kk = k[4, kmap[h]]
+        want = np.exp(g[4, h]) * (np.eye(d) - b[4, h] * np.outer(kk, kk))
+        if not np.allclose(P1[h], want, rtol=1e-14, atol=1e-15):
+            return False
+    # 4. beta = 0: only the decay acts, P = exp(sum g) I
+    P0 = fn(k, g, np.zeros_like(b), [3, 11], Hk, Hv)[0]
+    for h in range(Hv):
+        if not np.allclose(P0[h], np.exp(g[3:11, h].sum()) * np.eye(d), rtol=1e-13, atol=1e-15):
+            return False
+    # 5. a = 1, b = 1, unit k: one token is the projector I - k k^T (P P = P, P k = 0)
+    Pp = fn(k, np.zeros_like(g), np.ones_like(b), [7, 8], Hk, Hv)[0, 0]
+    return np.allclose(Pp @ Pp, Pp, atol=1e-14) and np.allclose(Pp @ k[7, 0], 0.0, atol=1e-14)
+
+
+def test_transition_pins_accept_the_oracle():
+    assert _transition_pins_pass(O.segment_transition)
+
+
+def _mutant_transition(kind):
+    def fn(k, g, beta, cu, Hk, Hv):
+        k = np.asarray(k, dtype=np.float64)
+        kmap = np.arange(Hv) // (Hv // Hk)
+        d = k.shape[-1]
+        out = np.zeros((len(cu) - 1, Hv, d, d))
+        for s in range(len(cu) - 1):
+            P = np.broadcast_to(np.eye(d), (Hv, d, d)).copy()
+            for t in range(cu[s], cu[s + 1]):
+                kt = k[t, kmap]
+                bb = np.ones(Hv) if kind == "beta_dropped" else np.asarray(beta)[t]
+                M = np.eye(d)[None] - bb[:, None, None] * kt[:, :, None] * kt[:, None, :]
+                a = np.ones(Hv) if kind == "decay_dropped" else np.exp(np.asarray(g)[t])
+                P = a[:, None, None] * (M @ P if kind == "reversed_order" else P @ M)
+            out[s] = P
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["reversed_order", "decay_dropped", "beta_dropped"])
+def test_transition_pins_catch_planted_mutation(kind):
+    assert not _transition_pins_pass(_mutant_transition(kind))
+
+
+def test_segment_bounds_split_whole_chunks():
+    # 300 tokens, chunks of 64 -> 5 chunks, 2 per segment: [0,128) [128,256) [256,300)
+    b = O.segment_bounds([0, 300], 3)
+    assert b[0].tolist() == [[0, 128], [128, 256], [256, 300]]
+    # more segments than chunks: trailing segments are empty, at the end
+    b = O.segment_bounds([10, 75], 4)
+    assert b[0].tolist() == [[10, 74], [74, 75], [75, 75], [75, 75]]
+    # an empty sequence gives empty segments at its offset
+    assert O.segment_bounds([5, 5], 2)[0].tolist() == [[5, 5], [5, 5]]
+    # the segments tile each sequence in order
+    cu = [0, 1, 64, 65, 500, 1000]
+    for nseg in (1, 2, 3, 7):
+        b = O.segment_bounds(cu, nseg)
+        for s in range(len(cu) - 1):
+            assert b[s, 0, 0] == cu[s] and b[s, -1, 1] == cu[s + 1]
+            assert np.all(b[s, 1:, 0] == b[s, :-1, 1])
+            nonempty = b[s, :, 1] > b[s, :, 0]
+            assert np.all((b[s, nonempty, 0] - cu[s]) % 64 == 0)
+
+
+@pytest.mark.parametrize("nseg", [1, 2, 3, 4, 9])
+def test_segmented_equals_per_token_rule(nseg):
+    Hk, Hv, d = 2, 4, 6
+    q, k, v, g, b = _seg_inputs(92, N=41, Hk=Hk, Hv=Hv, d=d)
+    S0 = np.random.default_rng(93).standard_normal((3, Hv, d, d))
+    cu, init = [0, 23, 23, 41], [1, 1, 0]
+    o1, s1 = O.delta_rule_recurrent(q, k, v, g, b, S0, init, cu, Hk, Hv)
+    o2, s2 = O.delta_rule_segmented(q, k, v, g, b, S0, init, cu, Hk, Hv, nseg, chunk_len=2)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s2, s1, rtol=1e-12, atol=1e-12)
+
+
+def test_segmented_form_depends_on_the_transition(monkeypatch):
+    # a wrong transition (here its transpose: the product in reverse order)
+    # must change the segmented result, so the equality above pins P too
+    Hk, Hv, d = 2, 4, 6
+    q, k, v, g, b = _seg_inputs(94, N=41, Hk=Hk, Hv=Hv, d=d)
+    S0 = np.random.default_rng(95).standard_normal((1, Hv, d, d))
+    good = O.delta_rule_segmented(q, k, v, g, b, S0, [1], [0, 41], Hk, Hv, 4, chunk_len=2)[1]
+    real = O.segment_transition
+    monkeypatch.setattr(O, "segment_transition", lambda *a: np.swapaxes(real(*a), -1, -2))
+    bad = O.delta_rule_segmented(q, k, v, g, b, S0, [1], [0, 41], Hk, Hv, 4, chunk_len=2)[1]
+    assert not np.allclose(bad, good, rtol=1e-6, atol=1e-6)
