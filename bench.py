@@ -277,7 +277,7 @@ def plan_verify(dev, fused=False):
     return p
 
 
-def plan_long(dev):
+def plan_long(dev, nseg=1):
     import torch
     from linear_attention_layers_amd import gdn, inputs
     lb = inputs.long_prefill()
@@ -290,12 +290,24 @@ def plan_long(dev):
                                                   chunks, True, y=d["y"]), conv_bytes(N, C, 2, 0, 1, True))
     p.add("postconv", lambda: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"], k=d["k"], v=d["v"]),
           postconv_bytes(N, C, 2))
-    p.add("prefill", lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                                        d["cu"], d["st"], d["hi"], o=d["o"]),
-          recurrence_bytes(N, Hk, Hv, 2, 0, 1), prefill_flops(lb))
+    if nseg == 1:
+        run = lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"],
+                                                 d["st"], d["hi"], o=d["o"])
+    else:
+        # the three launches of the segmented prefill are one stage; its
+        # bytes and flops are the unsegmented algorithm's
+        d["ws"] = torch.empty(gdn.gdn_prefill_segmented_workspace(1, Hv, nseg), dtype=torch.uint8,
+                              device=dev)
+        run = lambda: gdn.gdn_delta_rule_prefill_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                           d["cu"], d["st"], nseg, d["hi"], o=d["o"],
+                                                           workspace=d["ws"])
+    p.add("prefill", run, recurrence_bytes(N, Hk, Hv, 2, 0, 1), prefill_flops(lb))
     p.tokens = N
-    p.config = {"workload": "long_prefill_32k_bf16", "nseq": 1, "tokens": N, "channels": C,
-                "Hk": Hk, "Hv": Hv, "head_dim": 128, "layers": 1, "state_dtype": "f32", "seed": 4000}
+    p.config = {"workload": "long_prefill_32k_bf16" + (f"_seg{nseg}" if nseg > 1 else ""), "nseq": 1,
+                "tokens": N, "channels": C, "Hk": Hk, "Hv": Hv, "head_dim": 128, "layers": 1,
+                "state_dtype": "f32", "seed": 4000}
+    if nseg > 1:
+        p.config["segments"] = nseg
     p.keep = [d, chunks]
     return p
 
@@ -410,7 +422,7 @@ def plan_gates(dev):
 PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed,
          "verify-fused": lambda dev: plan_verify(dev, fused=True),
          "mixed-fused": lambda dev: plan_mixed(dev, fused=True), "out-norm": plan_out_norm,
-         "gates": plan_gates}
+         "gates": plan_gates, "long-seg": lambda dev: plan_long(dev, nseg=4)}
 
 
 def main():
@@ -430,7 +442,7 @@ def main():
               "multi-GPU runs are not part of this build)", file=sys.stderr)
         sys.exit(2)
     default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 10, "verify-fused": 20,
-                     "mixed-fused": 10, "out-norm": 20, "gates": 20}[args.workload]
+                     "mixed-fused": 10, "out-norm": 20, "gates": 20, "long-seg": 20}[args.workload]
     steps = args.steps if args.steps is not None else default_steps
     warmup = args.warmup if args.warmup is not None else max(2, steps // 10)
 

@@ -193,6 +193,39 @@ int gdn_delta_rule_prefill(const void* q, const void* k, const void* v, int act,
                            float* state, const uint8_t* has_initial_state,
                            void* o, void* stream);
 
+/* ---- 4b. segment-parallel prefill ----------------------------------------
+ * The prefill of item 4 with every sequence split into nseg segments of
+ * whole 64-token chunks, so that one long sequence occupies nseg times the
+ * workgroups.  The pages print no such form; it rests on the per-token rule
+ * being affine in the state (the gated delta rule of item 4): a run of tokens
+ * entering with S ends at S P + R, with P = M_1 ... M_n, M_t = a_t (I - b_t
+ * k_t k_t^T) (dk x dk, independent of v) and R the end state from S = 0.
+ * With n tokens and per = ceil(ceil(n / 64) / nseg), segment p covers tokens
+ * [bos + min(n, 64 p per), bos + min(n, 64 (p + 1) per)).  Three launches:
+ *   1. segment 0 from the entering state (its end state is X_1); each later
+ *      segment p from S = 0 (R_p) and, with v = 0, from S = I (P_p);
+ *   2. X_{p+1} = X_p P_p + R_p (float32), p = 1 .. nseg - 2;
+ *   3. each segment p >= 1 again from X_p: its o and, for the last one, the
+ *      final state.
+ * o and the final state equal item 4's up to rounding (the transitions carry
+ * the same bf16 operand rounding as the state does inside the prefill).
+ * Arguments as gdn_delta_rule_prefill, and
+ *   nseg       1..64; 1 runs gdn_delta_rule_prefill (no workspace needed);
+ *              nseg > 1 needs act = GDN_BF16 (GDN_ERR_DTYPE otherwise)
+ *   workspace  (device) at least gdn_prefill_segmented_workspace(nseq, Hv,
+ *              nseg) bytes, 16-byte aligned, owned by the caller, must not
+ *              overlap any argument (GDN_ERR_ALIAS); its contents on entry
+ *              are ignored, and on return it holds X, R and P, each
+ *              [nseq][nseg][Hv][dk][dk] float32 (index p = 0 unused). */
+size_t gdn_prefill_segmented_workspace(int nseq, int Hv, int nseg);
+int gdn_delta_rule_prefill_segmented(const void* q, const void* k, const void* v, int act,
+                                     const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int nseq, int N,
+                                     int Hk, int Hv, int dk, int dv,
+                                     float* state, const uint8_t* has_initial_state,
+                                     void* o, int nseg, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ---- 5. decode / verify step ---------------------------------------------
  * The same recurrence token by token with the state held in registers
  * ("Summary" item 3: state-resident per-token step).  Every sequence's

@@ -188,6 +188,41 @@ int gdn_delta_rule_prefill(const void* q, const void* k, const void* v, int act,
                   "delta_rule_prefill");
 }
 
+size_t gdn_prefill_segmented_workspace(int nseq, int Hv, int nseg) {
+  if (nseq <= 0 || Hv <= 0 || nseg <= 1) return 0;
+  return (size_t)3 * nseq * nseg * Hv * 128 * 128 * sizeof(float);
+}
+
+int gdn_delta_rule_prefill_segmented(const void* q, const void* k, const void* v, int act,
+                                     const float* g, const float* beta, const int32_t* cu, int nseq,
+                                     int N, int Hk, int Hv, int dk, int dv, float* state,
+                                     const uint8_t* has_init, void* o, int nseg, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  int st = check_recurrence(q, k, v, act, g, beta, cu, nseq, N, Hk, Hv, dk, dv, state, o);
+  if (st != GDN_OK) return st;
+  if (nseg < 1 || nseg > 64) return fail(GDN_ERR_SHAPE, "nseg must be in 1..64 (got %d)", nseg);
+  if (nseg == 1) return gdn_delta_rule_prefill(q, k, v, act, g, beta, cu, nseq, N, Hk, Hv, dk, dv, state,
+                                               has_init, o, stream);
+  if (act != GDN_BF16) return fail(GDN_ERR_DTYPE, "the segmented prefill needs bf16 activations");
+  if (nseq == 0) return GDN_OK;
+  if ((size_t)nseq * Hv * 2 * (2 * nseg - 1) > (size_t)INT32_MAX) return fail(GDN_ERR_SHAPE, "grid too large");
+  const size_t need = gdn_prefill_segmented_workspace(nseq, Hv, nseg);
+  if (!workspace) return fail(GDN_ERR_NULL, "workspace is required when nseg > 1");
+  if (!aligned16(workspace)) return fail(GDN_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(GDN_ERR_CAPACITY, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t e = elem_bytes(act);
+  const size_t nq = (size_t)N * Hk * dk * e, nv = (size_t)N * Hv * dv * e, ng = (size_t)N * Hv * 4;
+  const size_t ns = (size_t)nseq * Hv * dv * dk * 4;
+  if (overlaps(workspace, need, q, nq) || overlaps(workspace, need, k, nq) || overlaps(workspace, need, v, nv) ||
+      overlaps(workspace, need, g, ng) || overlaps(workspace, need, beta, ng) ||
+      overlaps(workspace, need, o, nv) || overlaps(workspace, need, state, ns))
+    return fail(GDN_ERR_ALIAS, "workspace must not overlap q, k, v, g, beta, o or state");
+  return launched(gdn::launch_prefill_segmented(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, nseg,
+                                                static_cast<float*>(workspace), as_stream(stream)),
+                  "delta_rule_prefill_segmented");
+}
+
 int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act, const float* g,
                         const float* beta, const int32_t* cu, int nseq, int N, int Hk, int Hv,
                         int dk, int dv, float* state, const uint8_t* has_init, void* o,

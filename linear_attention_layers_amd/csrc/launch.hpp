@@ -39,6 +39,13 @@ hipError_t launch_commit(const gdn_layer_io* layers, int L, const int32_t* cu,
                          const int32_t* n_keep, const uint8_t* has_init, int nseq, int C,
                          int Hk, int Hv, int act, hipStream_t st);
 
+// Segment-parallel prefill (bf16 activations): two passes of the
+// warp-specialised prefill with the segment chain between them; ws holds
+// 3 * nseq * nseg * Hv float32 128 x 128 matrices.
+hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
+                                    float* state, const uint8_t* has_init, void* o, int nseg,
+                                    float* ws, hipStream_t st);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int act, const float* g,
                           const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
                           float* state, const uint8_t* has_init, void* o, hipStream_t st);

@@ -470,11 +470,24 @@ __device__ __forceinline__ Prec<uint16_t>::F32 kq_fragT(const uint16_t* p, int c
   return f;
 }
 
-template <int VB>
+// Segment roles (SEG != 0).  A sequence is split into nseg segments of
+// whole chunks (segment p: tokens [bos + min(n, p per 64), bos + min(n,
+// (p + 1) per 64)), per = ceil(ceil(n / 64) / nseg)).  The per-token rule is
+// affine in the state, S_end = S_start P + R, so
+//   SEG = 1 (first pass): segment 0 runs from the entering state and writes
+//     its end state to X[1]; every later segment p runs twice over its
+//     tokens, from S = 0 (end state R[p]) and, with v = 0, from S = I (end
+//     state P[p], dk x dk); neither writes o;
+//   SEG = 2 (second pass): every segment p >= 1 runs from X[p], written by
+//     the combine X[p+1] = X[p] P[p] + R[p]; it writes o, and the last one
+//     the final state.
+// The workspace holds X, R and P, each [nseq][nseg][Hv][128][128] float32.
+template <int VB, int SEG>
 __global__ __launch_bounds__(512) void prefill_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-    int Hk, int Hv, float* state, const uint8_t* __restrict__ has_init, uint16_t* __restrict__ o) {
+    int Hk, int Hv, float* state, const uint8_t* __restrict__ has_init, uint16_t* __restrict__ o,
+    int nseg, float* ws) {
   using PR = Prec<uint16_t>;
   constexpr int DVS = 64 * VB;   // state rows per workgroup (4 consumer waves)
   constexpr int NSL = DK / DVS;
@@ -496,12 +509,21 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
   // i = (b % 8) * (items / 8) + b / 8 keeps the heads sharing a k-head, which
   // read the same K and Q, on one XCD and its L2.
   const int items = Hv * NSL;
-  const int nseq = gridDim.x / items;
-  const int rank = blockIdx.x / items;
+  // groups of `items` workgroups per sequence: 1 (plain), 2 nseg - 1 (first
+  // segment pass: segment 0, then R and P of each later segment), nseg - 1
+  // (second pass)
+  const int groups = SEG == 0 ? 1 : SEG == 1 ? 2 * nseg - 1 : nseg - 1;
+  const int nseq = gridDim.x / (items * groups);
+  const int rank = blockIdx.x / (items * groups);
+  const int grp = blockIdx.x / items % groups;
   int item = blockIdx.x % items;
   if ((items & 7) == 0) item = (item & 7) * (items >> 3) + (item >> 3);
+  // segment p and role: 0 = the real rows, 1 = R (from 0, no o), 2 = P
+  // (from I, v = 0, no o)
+  const int p = SEG == 0 ? 0 : SEG == 1 ? (grp + 1) / 2 : grp + 1;
+  const int role = SEG == 1 && grp > 0 ? 2 - (grp & 1) : 0;
   int s = rank;
-  if (nseq > 1 && nseq <= kOrderMax) {
+  if (SEG == 0 && nseq > 1 && nseq <= kOrderMax) {
     if (tid < nseq) sm.len[tid] = cu[tid + 1] - cu[tid];
     __syncthreads();
     if (tid < nseq) {
@@ -519,15 +541,27 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
   const int slice = item % NSL;
   const int h = item / NSL;
   const int kh = h / (Hv / Hk);
-  const int bos = cu[s], eos = cu[s + 1];
+  int bos = cu[s], eos = cu[s + 1];
   const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
+  if (SEG != 0) {
+    const int n = eos - bos, per = ((n + BT - 1) / BT + nseg - 1) / nseg;
+    eos = bos + min(n, (p + 1) * per * BT);
+    bos = bos + min(n, p * per * BT);
+  }
   const int nc = eos > bos ? (eos - bos + BT - 1) / BT : 0;
   // valid tokens of chunk c (0 past the end)
   auto chunk_len = [&](int c) { return max(0, min(BT, eos - (bos + BT * c))); };
 
+  // the transition roles of the first segment pass write no o: their
+  // workgroups run a body without the Q side (no Q tiles, Q K^T pairs, P,
+  // Q S^T, P U or o stores)
+  const bool o_on_wg = !(SEG == 1 && p > 0);
+
   if (wave >= 4) {
     // ================================================================ producers
     if (nc == 0) return;
+    auto produce = [&](auto wo_c) __attribute__((always_inline)) {
+    constexpr bool WO = decltype(wo_c)::value;
     const int ptid = tid - 256;
     u32x4 pk[KQ_ITEMS], pq[KQ_ITEMS];
     float gr = 0.f, br = 0.f;
@@ -541,7 +575,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         const int idx = ptid + 256 * it;
         const int off = (((idx >> 4) * Hk + kh) * DK + (idx & 15) * 8) * 2;
         pk[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-        pq[it] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        if constexpr (WO) pq[it] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
       }
     };
     auto stage_kq = [&](int buf) {
@@ -550,7 +584,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         const int idx = ptid + 256 * it;
         const int e = kq_at(idx >> 4, 2 * (idx & 15));
         *reinterpret_cast<u32x4*>(&sm.K[buf][e]) = pk[it];
-        *reinterpret_cast<u32x4*>(&sm.Q[buf][e]) = pq[it];
+        if constexpr (WO) *reinterpret_cast<u32x4*>(&sm.Q[buf][e]) = pq[it];
       }
     };
     // gate vectors: one token per lane (wave rw == 3 only, which forms two tile pairs, not three)
@@ -589,7 +623,8 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         pv[e] = dec * qk[e];
         av[e] = j0 + e < i ? bti * dec * kk[e] : 0.f;
       }
-      *reinterpret_cast<u32x2*>(&sm.P[ab][i * LDT + j0]) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+      if constexpr (WO)
+        *reinterpret_cast<u32x2*>(&sm.P[ab][i * LDT + j0]) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
       if (diag)
         *reinterpret_cast<float4*>(&sm.Ad[rw][r16][4 * kg]) = make_float4(av[0], av[1], av[2], av[3]);
       else
@@ -613,20 +648,24 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const auto d0 = kq_frag(Kb, 16 * bd + r16, 32 * t, kg);
-        const auto q0 = kq_frag(Qb, 16 * bd + r16, 32 * t, kg);
         const auto b1 = kq_frag(Kb, 16 * bj1 + r16, 32 * t, kg);
         const auto a1 = kq_frag(Kb, 16 * bi1 + r16, 32 * t, kg);
-        const auto q1 = kq_frag(Qb, 16 * bi1 + r16, 32 * t, kg);
         kk0 = PR::mma32(d0, d0, kk0);
-        qk0 = PR::mma32(d0, q0, qk0);
         kk1 = PR::mma32(b1, a1, kk1);
-        qk1 = PR::mma32(b1, q1, qk1);
+        if constexpr (WO) {
+          const auto q0 = kq_frag(Qb, 16 * bd + r16, 32 * t, kg);
+          const auto q1 = kq_frag(Qb, 16 * bi1 + r16, 32 * t, kg);
+          qk0 = PR::mma32(d0, q0, qk0);
+          qk1 = PR::mma32(b1, q1, qk1);
+        }
         if constexpr (kThird) {
           const auto b2 = kq_frag(Kb, 16 * bj2 + r16, 32 * t, kg);
           const auto a2 = kq_frag(Kb, 16 * bi2 + r16, 32 * t, kg);
-          const auto q2 = kq_frag(Qb, 16 * bi2 + r16, 32 * t, kg);
           kk2 = PR::mma32(b2, a2, kk2);
-          qk2 = PR::mma32(b2, q2, qk2);
+          if constexpr (WO) {
+            const auto q2 = kq_frag(Qb, 16 * bi2 + r16, 32 * t, kg);
+            qk2 = PR::mma32(b2, q2, qk2);
+          }
         }
       }
       pair_store(true, bd, bd, kk0, qk0, kb, ab);
@@ -695,6 +734,13 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       factors(c + 1);
       __syncthreads();
     }
+    };
+    if constexpr (SEG == 1) {
+      if (o_on_wg) produce(std::true_type{});
+      else produce(std::false_type{});
+    } else {
+      produce(std::true_type{});
+    }
     return;
   }
 
@@ -705,26 +751,52 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
   for (int b = 0; b < VB; ++b) v0[b] = slice * DVS + 16 * (w * VB + b);
 
   f32x4 st[VB][8];
+  // entering state (src; none = zero, or the identity for a P role) and
+  // where the end state goes (dst; none = not written)
   float* const sbase = state + ((int64_t)s * Hv + h) * (DK * DK);
+  const float* src = init ? sbase : nullptr;
+  float* dst = sbase;
+  bool ident = false, v_on = true, o_on = true;
+  if (SEG != 0) {
+    auto wsp = [&](int which, int pp) {
+      return ws + ((((int64_t)which * nseq + s) * nseg + pp) * Hv + h) * (DK * DK);
+    };
+    if (SEG == 1 && p == 0) {
+      dst = wsp(0, 1);
+    } else if (SEG == 1) {
+      src = nullptr;
+      dst = wsp(role, p);
+      ident = role == 2;
+      v_on = role == 1;
+      o_on = false;
+    } else {
+      src = wsp(0, p);
+      dst = p == nseg - 1 ? sbase : nullptr;
+    }
+  }
 #pragma unroll
   for (int b = 0; b < VB; ++b)
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
-      if (init) {
-        const float4 t = *reinterpret_cast<const float4*>(sbase + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg);
+      if (src != nullptr) {
+        const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg);
         st[b][cb] = f32x4{t.x, t.y, t.z, t.w};
       } else {
-        st[b][cb] = zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[b][cb][e] = ident && v0[b] + r16 == 16 * cb + 4 * kg + e ? 1.f : 0.f;
       }
     }
 
   if (nc > 0) {
+    // a compile-time constant except in the first segment pass, where it is
+    // uniform over the workgroup
+    const bool WO = o_on_wg;
     // V of one chunk in the accumulator layout: lane holds tokens
     // 16 ib + 4 kg + e of state row v0 + r16
     uint16_t vr[VB][4][4];
     auto load_v = [&](int c) {
       const int64_t c0 = bos + BT * c;
-      const auto rv = buf_rsrc(v + c0 * Hv * DK, chunk_len(c) * Hv * DK * 2);
+      const auto rv = buf_rsrc(v + c0 * Hv * DK, v_on ? chunk_len(c) * Hv * DK * 2 : 0);
 #pragma unroll
       for (int b = 0; b < VB; ++b)
 #pragma unroll
@@ -774,7 +846,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
           for (int e = 0; e < 4; ++e) vv[b][ib][e] = bf16_to_f32(vr[b][ib][e]);
-      store_o();
+      if (WO) store_o();
       load_v(c + 1);
 
       // The chain of the chunk is Z -> R -> the four block steps of the
@@ -880,7 +952,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
 #pragma unroll
         for (int b = 0; b < VB; ++b) uu[b][0] = PR::mma16(td, PR::reg16(rr[b][0]), zero4());
       }
-      qs_step(0);
+      if (WO) qs_step(0);
       {
         const auto am = PR::lds16(ATc, LDT, 16 + r16, 0, kg);
         const auto td = PR::lds16(ATc, LDT, 16 + r16, 16, kg);
@@ -890,7 +962,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           uu[b][1] = PR::mma16(td, PR::reg16(rr[b][1]), zero4());
         }
       }
-      qs_step(1);
+      if (WO) qs_step(1);
       {
         // blocks 0 and 1 are final: first half of the state update and
         // their part of O
@@ -913,14 +985,16 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           rr[b][2] = PR::mma32(a2, u01[b], rr[b][2]);
           rr[b][3] = PR::mma32(a3, u01[b], rr[b][3]);
         }
-        const auto p0 = PR::lds16(Pc, LDT, r16, 0, kg);
+        if (WO) {
+          const auto p0 = PR::lds16(Pc, LDT, r16, 0, kg);
 #pragma unroll
-        for (int b = 0; b < VB; ++b) pu[b][0] = PR::mma16(PR::reg16(uu[b][0]), p0, zero4());
+          for (int b = 0; b < VB; ++b) pu[b][0] = PR::mma16(PR::reg16(uu[b][0]), p0, zero4());
 #pragma unroll
-        for (int ib = 1; ib < 4; ++ib) {
-          const auto p01 = PR::lds32(Pc, LDT, 16 * ib + r16, 0, kg);
+          for (int ib = 1; ib < 4; ++ib) {
+            const auto p01 = PR::lds32(Pc, LDT, 16 * ib + r16, 0, kg);
 #pragma unroll
-          for (int b = 0; b < VB; ++b) pu[b][ib] = PR::mma32(u01[b], p01, zero4());
+            for (int b = 0; b < VB; ++b) pu[b][ib] = PR::mma32(u01[b], p01, zero4());
+          }
         }
         state_half(0, du, true);
       }
@@ -929,7 +1003,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
 #pragma unroll
         for (int b = 0; b < VB; ++b) uu[b][2] = PR::mma16(td, PR::reg16(rr[b][2]), zero4());
       }
-      qs_step(2);
+      if (WO) qs_step(2);
       {
         const auto am = PR::lds16(ATc, LDT, 48 + r16, 32, kg);
         const auto td = PR::lds16(ATc, LDT, 48 + r16, 48, kg);
@@ -941,7 +1015,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           uu[b][3] = PR::mma16(td, PR::reg16(rr[b][3]), zero4());
         }
       }
-      qs_step(3);
+      if (WO) qs_step(3);
       {
         // blocks 2 and 3: second half of the state update and the rest of O
         typename PR::F32 du[VB], u23[VB];
@@ -957,53 +1031,107 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           u23[b] = PR::reg32(uu[b][2], uu[b][3]);
         }
         state_half(32, du, false);
-        const auto p2 = PR::lds16(Pc, LDT, 32 + r16, 32, kg);
-        const auto p3 = PR::lds32(Pc, LDT, 48 + r16, 32, kg);
+        if (WO) {
+          const auto p2 = PR::lds16(Pc, LDT, 32 + r16, 32, kg);
+          const auto p3 = PR::lds32(Pc, LDT, 48 + r16, 32, kg);
 #pragma unroll
-        for (int b = 0; b < VB; ++b) {
-          const f32x4 t2 = PR::mma16(PR::reg16(uu[b][2]), p2, zero4());
+          for (int b = 0; b < VB; ++b) {
+            const f32x4 t2 = PR::mma16(PR::reg16(uu[b][2]), p2, zero4());
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pu[b][2][e] += t2[e];
-          pu[b][3] = PR::mma32(u23[b], p3, pu[b][3]);
+            for (int e = 0; e < 4; ++e) pu[b][2][e] += t2[e];
+            pu[b][3] = PR::mma32(u23[b], p3, pu[b][3]);
+          }
         }
       }
 
-      // ---- O^T = (Q S0^T)^T diag(gamma) + U^T P^T; lane: token 16 ib + r16,
-      // state rows v0 + 4 kg .. +3
-      ro_prev = buf_rsrc(o + c0 * Hv * DK, n * Hv * DK * 2);
+      if (WO) {
+        // ---- O^T = (Q S0^T)^T diag(gamma) + U^T P^T; lane: token 16 ib + r16,
+        // state rows v0 + 4 kg .. +3
+        ro_prev = buf_rsrc(o + c0 * Hv * DK, o_on ? n * Hv * DK * 2 : 0);
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const float gt = Wc[BT + 16 * ib + r16];
+        for (int ib = 0; ib < 4; ++ib) {
+          const float gt = Wc[BT + 16 * ib + r16];
 #pragma unroll
-        for (int b = 0; b < VB; ++b) {
-          float ov[4];
+          for (int b = 0; b < VB; ++b) {
+            float ov[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = gt * qt[b][ib][e] + pu[b][ib][e];
-          opk[b][ib] = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+            for (int e = 0; e < 4; ++e) ov[e] = gt * qt[b][ib][e] + pu[b][ib][e];
+            opk[b][ib] = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+          }
         }
       }
       __syncthreads();
     }
-    store_o();
+    if (WO) store_o();
   }
 
+  if (dst != nullptr) {
 #pragma unroll
-  for (int b = 0; b < VB; ++b)
+    for (int b = 0; b < VB; ++b)
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-      *reinterpret_cast<float4*>(sbase + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg) =
-          make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
+      for (int cb = 0; cb < 8; ++cb)
+        *reinterpret_cast<float4*>(dst + (int64_t)(v0[b] + r16) * DK + 16 * cb + 4 * kg) =
+            make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
+  }
 }
 
-template <int VB>
+template <int VB, int SEG>
 hipError_t launch_ws(const void* q, const void* k, const void* v, const float* g, const float* beta,
                      const int32_t* cu, int nseq, int Hk, int Hv, float* state,
-                     const uint8_t* has_init, void* o, hipStream_t st) {
-  const dim3 grid(nseq * Hv * (DK / (64 * VB)));
-  hipLaunchKernelGGL((prefill_ws_kernel<VB>), grid, dim3(512), 0, st, static_cast<const uint16_t*>(q),
+                     const uint8_t* has_init, void* o, int nseg, float* ws, hipStream_t st) {
+  const int groups = SEG == 0 ? 1 : SEG == 1 ? 2 * nseg - 1 : nseg - 1;
+  const dim3 grid(nseq * Hv * (DK / (64 * VB)) * groups);
+  hipLaunchKernelGGL((prefill_ws_kernel<VB, SEG>), grid, dim3(512), 0, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), g, beta, cu, Hk,
-                     Hv, state, has_init, static_cast<uint16_t*>(o));
+                     Hv, state, has_init, static_cast<uint16_t*>(o), nseg, ws);
   return hipGetLastError();
+}
+
+// The segment chain X[p + 1] = X[p] P[p] + R[p], p = 1 .. nseg - 2, for one
+// 16-row block of one (sequence, v-head).  Rows of the chain are
+// independent (row i of X[p + 1] needs row i of X[p] and all of P[p]), so
+// every block runs its own chain.  Thread (r, cg) forms row 16 rb + r,
+// columns 8 cg .. 8 cg + 7, in float32 with the products added in k order.
+__global__ __launch_bounds__(256) void seg_combine_kernel(float* ws, int nseq, int nseg, int Hv) {
+  __shared__ float Pl[DK * DK];
+  __shared__ float Xl[16 * DK];
+  const int rb = blockIdx.x & 7, h = (blockIdx.x >> 3) % Hv, s = (blockIdx.x >> 3) / Hv;
+  const int tid = threadIdx.x, r = tid >> 4, cg = tid & 15;
+  const int row = 16 * rb + r;
+  auto wsp = [&](int which, int pp) {
+    return ws + ((((int64_t)which * nseq + s) * nseg + pp) * Hv + h) * (DK * DK);
+  };
+  auto load8 = [](const float* p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  };
+  float x[8];
+  load8(wsp(0, 1) + row * DK + 8 * cg, x);
+  for (int p = 1; p + 1 < nseg; ++p) {
+    __syncthreads();   // the previous step is done with Pl and Xl
+    const float4* Pp = reinterpret_cast<const float4*>(wsp(2, p));
+#pragma unroll 4
+    for (int i = tid; i < DK * DK / 4; i += 256) reinterpret_cast<float4*>(Pl)[i] = Pp[i];
+    *reinterpret_cast<float4*>(&Xl[r * DK + 8 * cg]) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(&Xl[r * DK + 8 * cg + 4]) = make_float4(x[4], x[5], x[6], x[7]);
+    __syncthreads();
+    float acc[8];
+    load8(wsp(1, p) + row * DK + 8 * cg, acc);
+    for (int kk = 0; kk < DK; ++kk) {
+      const float xv = Xl[r * DK + kk];
+      const float4 p0 = *reinterpret_cast<const float4*>(&Pl[kk * DK + 8 * cg]);
+      const float4 p1 = *reinterpret_cast<const float4*>(&Pl[kk * DK + 8 * cg + 4]);
+      acc[0] = __builtin_fmaf(xv, p0.x, acc[0]); acc[1] = __builtin_fmaf(xv, p0.y, acc[1]);
+      acc[2] = __builtin_fmaf(xv, p0.z, acc[2]); acc[3] = __builtin_fmaf(xv, p0.w, acc[3]);
+      acc[4] = __builtin_fmaf(xv, p1.x, acc[4]); acc[5] = __builtin_fmaf(xv, p1.y, acc[5]);
+      acc[6] = __builtin_fmaf(xv, p1.z, acc[6]); acc[7] = __builtin_fmaf(xv, p1.w, acc[7]);
+    }
+    float* Xn = wsp(0, p + 1) + row * DK + 8 * cg;
+    *reinterpret_cast<float4*>(Xn) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(Xn + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = acc[i];
+  }
 }
 
 template <class T, int NW, int VB>
@@ -1019,13 +1147,27 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const float* g,
 
 }  // namespace
 
+hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
+                                    float* state, const uint8_t* has_init, void* o, int nseg,
+                                    float* ws, hipStream_t st) {
+  hipError_t e = launch_ws<1, 1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, nseg, ws, st);
+  if (e != hipSuccess) return e;
+  if (nseg > 2) {
+    hipLaunchKernelGGL(seg_combine_kernel, dim3(nseq * Hv * 8), dim3(256), 0, st, ws, nseq, nseg, Hv);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_ws<1, 2>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, nseg, ws, st);
+}
+
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int act, const float* g,
                           const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
                           float* state, const uint8_t* has_init, void* o, hipStream_t st) {
   // float32 activations take the single-role schedule: three K/Q buffers of
   // 4-byte elements do not fit in LDS.
   if (act == GDN_F32) return launch_t<float, 4, 1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
-  return launch_ws<1>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, st);
+  return launch_ws<1, 0>(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, 1, nullptr, st);
 }
 
 }  // namespace gdn

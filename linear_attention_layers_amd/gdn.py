@@ -77,6 +77,10 @@ _postconv = _sig("gdn_postconv_l2", [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _i
                                      _vp, _vp, _i32, _vp])
 _prefill = _sig("gdn_delta_rule_prefill", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _vp, _vp, _vp, _vp])
+_seg_ws = _sig("gdn_prefill_segmented_workspace", [_i32, _i32, _i32], ctypes.c_size_t)
+_prefill_seg = _sig("gdn_delta_rule_prefill_segmented", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32,
+                                                         _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
+                                                         ctypes.c_size_t, _vp])
 _step = _sig("gdn_delta_rule_step", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _vp, _vp, _vp, _i32, _vp])
 _commit = _sig("gdn_commit", [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -90,7 +94,8 @@ _gates = _sig("gdn_gates", [_vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp])
 
 EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
             "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd",
-            "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_delta_rule_step", "gdn_commit",
+            "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_prefill_segmented_workspace",
+            "gdn_delta_rule_prefill_segmented", "gdn_delta_rule_step", "gdn_commit",
             "gdn_decode_fused", "gdn_out_norm", "gdn_gates"]
 
 
@@ -256,6 +261,31 @@ def gdn_delta_rule_prefill(q, k, v, g, beta, cu_seqlens, state, has_initial_stat
     _check(_prefill(_ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(g), _ptr(beta),
                     _ptr(cu_seqlens), nseq, N, Hk, Hv, dk, dv, _ptr(state),
                     _ptr(has_initial_state), _ptr(o), _stream(stream)), "gdn_delta_rule_prefill")
+    return o
+
+
+def gdn_prefill_segmented_workspace(nseq: int, Hv: int, nseg: int) -> int:
+    """Workspace bytes gdn_delta_rule_prefill_segmented needs (0 for nseg <= 1)."""
+    return int(_seg_ws(nseq, Hv, nseg))
+
+
+def gdn_delta_rule_prefill_segmented(q, k, v, g, beta, cu_seqlens, state, nseg: int,
+                                     has_initial_state=None, o: Optional[torch.Tensor] = None,
+                                     workspace: Optional[torch.Tensor] = None,
+                                     stream=None) -> torch.Tensor:
+    """Prefill with every sequence split into nseg segments (C ABI
+    gdn_delta_rule_prefill_segmented).  workspace: a device byte tensor of at
+    least gdn_prefill_segmented_workspace(nseq, Hv, nseg) bytes (allocated
+    here when not given)."""
+    N, Hk, Hv, dk, dv, nseq, o = _recurrence_args(q, k, v, g, beta, cu_seqlens, state, o)
+    need = gdn_prefill_segmented_workspace(nseq, Hv, nseg)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_prefill_seg(_ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(g), _ptr(beta),
+                        _ptr(cu_seqlens), nseq, N, Hk, Hv, dk, dv, _ptr(state),
+                        _ptr(has_initial_state), _ptr(o), nseg, _ptr(workspace), nbytes,
+                        _stream(stream)), "gdn_delta_rule_prefill_segmented")
     return o
 
 

@@ -174,6 +174,38 @@ def test_recurrence_validation():
     assert step(*(a[:-1] + [1, None])) == SHAPE
 
 
+def test_prefill_segmented_validation():
+    wsz = lib.gdn_prefill_segmented_workspace
+    wsz.restype = ctypes.c_size_t
+    wsz.argtypes = [i32, i32, i32]
+    assert wsz(2, 4, 3) == 3 * 2 * 3 * 4 * 128 * 128 * 4
+    assert wsz(2, 4, 1) == 0 and wsz(0, 4, 3) == 0
+    fn = lib.gdn_delta_rule_prefill_segmented
+    fn.restype = i32
+    fn.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp,
+                   ctypes.c_size_t, vp]
+    need = wsz(2, 4, 3)
+    base = [FAKE, FAKE + (1 << 24), FAKE + (2 << 24), 1, FAKE + (3 << 24), FAKE + (4 << 24),
+            FAKE + (5 << 24), 2, 100, 2, 4, 128, 128, FAKE + (6 << 24), None, FAKE + (7 << 24),
+            3, FAKE + (1 << 30), need, None]
+
+    def call(**kw):
+        a = list(base)
+        idx = {"act": 3, "Hv": 10, "nseg": 16, "ws": 17, "wsb": 18}
+        for k_, v_ in kw.items():
+            a[idx[k_]] = v_
+        return fn(*a)
+
+    assert call(Hv=3) == SHAPE
+    assert call(nseg=0) == SHAPE and call(nseg=65) == SHAPE
+    assert call(act=0) == DTYPE                      # float32 activations: unsegmented only
+    assert call(ws=None) == NULL
+    assert call(ws=FAKE + (1 << 30) + 4) == ALIGN
+    assert call(wsb=need - 1) == CAPACITY
+    assert call(ws=FAKE + (2 << 24)) == ALIAS        # workspace over v
+    assert call(ws=FAKE + (6 << 24) - 4096) == ALIAS   # workspace running into state
+
+
 def test_commit_validation():
     fn = lib.gdn_commit
     fn.restype = i32

@@ -143,6 +143,20 @@ def test_long_prefill_32k_sampled():
     _check_recurrence(lb, out, [31], TL.REC_BF16)
 
 
+def test_long_prefill_32k_segmented_sampled():
+    # the segmented prefill at the benchmark's launch configuration (4
+    # segments of 8192 tokens), from the same q, k, v as the plain prefill
+    lb = I.long_prefill()
+    out = TL.gpu_layer(lb)
+    st = lb.state.to(DEV).contiguous()
+    o = gdn.gdn_delta_rule_prefill_segmented(out["q"], out["k"], out["v"], out["g"], out["beta"],
+                                             out["cu"], st, 4, out["hi"])
+    torch.cuda.synchronize()
+    seg = dict(out, o=o, state=st)
+    _check_recurrence(lb, seg, [0, 1], TL.REC_BF16)
+    _check_recurrence(lb, seg, [31], TL.REC_BF16)
+
+
 def test_spec_verify_36_layers_then_one_commit():
     L = 36
     layers, runs = [], []
