@@ -50,6 +50,7 @@ METRIC = "GDN layer tokens/s (conv+postconv+delta-rule) and % of HBM roofline, 1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_varlen_prefill_bf16.json")
 KERNEL_SOURCES = {
     "conv": ["conv.hip", "device_common.hpp"],
+    "convpost": ["conv.hip", "device_common.hpp"],
     "postconv": ["postconv.hip", "device_common.hpp"],
     "prefill": ["prefill.hip", "mfma.hpp", "device_common.hpp"],
     "step": ["step.hip", "mfma.hpp", "device_common.hpp"],
@@ -81,6 +82,24 @@ def conv_bytes(N, C, e, n_init, nseq, write_state):
 
 def postconv_bytes(N, C, e):
     return 2 * N * C * e
+
+
+# The conv and the post-conv run as one launch (gdn_conv_postconv_fwd) unless
+# --split-conv asks for the two separate launches.  The fused launch moves
+# conv_bytes: x in, q|k|v (N x C) out instead of y.
+SPLIT_CONV = False
+
+
+def add_conv_post(p, x, w, cs, hi, cu, chunks, write_state, Hk, Hv, N, C, n_init, nseq, y, q, k, v):
+    from linear_attention_layers_amd import gdn
+    if SPLIT_CONV:
+        p.add("conv", lambda: gdn.gdn_causal_conv_fwd(x, w, None, cs, hi, cu, chunks, write_state, y=y),
+              conv_bytes(N, C, 2, n_init, nseq, write_state))
+        p.add("postconv", lambda: gdn.gdn_postconv_l2(y, Hk, Hv, 1e-6, q=q, k=k, v=v), postconv_bytes(N, C, 2))
+    else:
+        p.add("convpost", lambda: gdn.gdn_conv_postconv_fwd(x, w, None, cs, hi, cu, chunks, write_state, Hk, Hv,
+                                                            1e-6, q=q, k=k, v=v),
+              conv_bytes(N, C, 2, n_init, nseq, write_state))
 
 
 def recurrence_bytes(N, Hk, Hv, e, n_state_read, n_state_write):
@@ -117,6 +136,7 @@ def algorithmic_bytes(lb) -> dict:
     n_init = int(lb.has_init.sum())
     return {"conv": conv_bytes(N, C, e, n_init, lb.nseq, True),
             "postconv": postconv_bytes(N, C, e),
+            "convpost": conv_bytes(N, C, e, n_init, lb.nseq, True),
             "prefill": recurrence_bytes(N, lb.geo.Hk, lb.geo.Hv, e, n_init, lb.nseq)}
 
 
@@ -210,10 +230,8 @@ def plan_varlen(dev):
     algo = algorithmic_bytes(lb)
     p = Plan()
     p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
-    p.add("conv", lambda: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], d["hi"], d["cu"],
-                                                  chunks, True, y=d["y"]), algo["conv"])
-    p.add("postconv", lambda: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"], k=d["k"], v=d["v"]),
-          algo["postconv"])
+    add_conv_post(p, d["x"], d["w"], d["cs"], d["hi"], d["cu"], chunks, True, Hk, Hv, N, lb.geo.C,
+                  int(lb.has_init.sum()), lb.nseq, d["y"], d["q"], d["k"], d["v"])
     p.add("prefill", lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                         d["cu"], d["st"], d["hi"], o=d["o"]),
           algo["prefill"], prefill_flops(lb))
@@ -249,12 +267,8 @@ def plan_verify(dev, fused=False):
                       v_out=d["v"]),
                   fused_bytes(N, C, Hk, Hv, 2, lb.nseq, False, 0, True))
         else:
-            p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None,
-                                                             d["cu"], d["chunks"], False, y=d["y"]),
-                  conv_bytes(N, C, 2, lb.nseq, lb.nseq, False))
-            p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6,
-                                                                             q=d["q"], k=d["k"], v=d["v"]),
-                  postconv_bytes(N, C, 2))
+            add_conv_post(p, d["x"], d["w"], d["cs"], None, d["cu"], d["chunks"], False, Hk, Hv, N, C,
+                          lb.nseq, lb.nseq, d["y"], d["q"], d["k"], d["v"])
             p.add("step", lambda d=d: gdn.gdn_delta_rule_step(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                               d["cu"], d["st"], None, o=d["o"],
                                                               commit_state=False),
@@ -286,10 +300,8 @@ def plan_long(dev, nseg=1):
     chunks = torch.empty(gdn.gdn_chunk_capacity(N, lb.nseq), 4, dtype=torch.int32, device=dev)
     p = Plan()
     p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
-    p.add("conv", lambda: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], d["hi"], d["cu"],
-                                                  chunks, True, y=d["y"]), conv_bytes(N, C, 2, 0, 1, True))
-    p.add("postconv", lambda: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6, q=d["q"], k=d["k"], v=d["v"]),
-          postconv_bytes(N, C, 2))
+    add_conv_post(p, d["x"], d["w"], d["cs"], d["hi"], d["cu"], chunks, True, Hk, Hv, N, C, 0, 1, d["y"],
+                  d["q"], d["k"], d["v"])
     if nseg == 1:
         run = lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"],
                                                  d["st"], d["hi"], o=d["o"])
@@ -330,20 +342,12 @@ def plan_mixed(dev, fused=False):
             # conv and post-conv over the prefill tokens only; the decode
             # tokens go through the fused launch
             d["chunks_pre"] = gdn.gdn_make_chunks_device(d["cu_pre"], Npre)
-            p.add("conv", lambda d=d, n=Npre, m=npre: gdn.gdn_causal_conv_fwd(
-                      d["x"][:n], d["w"], None, d["cs"][:m], None, d["cu_pre"], d["chunks_pre"], True,
-                      y=d["y"][:n]),
-                  conv_bytes(Npre, C, 2, npre, npre, True))
-            p.add("postconv", lambda d=d, n=Npre, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(
-                      d["y"][:n], Hk, Hv, 1e-6, q=d["q"][:n], k=d["k"][:n], v=d["v"][:n]),
-                  postconv_bytes(Npre, C, 2))
+            add_conv_post(p, d["x"][:Npre], d["w"], d["cs"][:npre], None, d["cu_pre"], d["chunks_pre"], True,
+                          Hk, Hv, Npre, C, npre, npre, d["y"][:Npre], d["q"][:Npre], d["k"][:Npre],
+                          d["v"][:Npre])
         else:
-            p.add("conv", lambda d=d: gdn.gdn_causal_conv_fwd(d["x"], d["w"], None, d["cs"], None,
-                                                             d["cu"], d["chunks"], True, y=d["y"]),
-                  conv_bytes(N, C, 2, lb.nseq, lb.nseq, True))
-            p.add("postconv", lambda d=d, Hk=Hk, Hv=Hv: gdn.gdn_postconv_l2(d["y"], Hk, Hv, 1e-6,
-                                                                             q=d["q"], k=d["k"], v=d["v"]),
-                  postconv_bytes(N, C, 2))
+            add_conv_post(p, d["x"], d["w"], d["cs"], None, d["cu"], d["chunks"], True, Hk, Hv, N, C,
+                          lb.nseq, lb.nseq, d["y"], d["q"], d["k"], d["v"])
         p.add("prefill", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_prefill(
                   d["q"][:n], d["k"][:n], d["v"][:n], d["g"][:n], d["beta"][:n], d["cu_pre"],
                   d["st"][:m], None, o=d["o"][:n]),
@@ -432,6 +436,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", choices=sorted(PLANS), default="varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-conv", action="store_true",
+                    help="run the conv and the post-conv as two launches instead of the fused one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -461,6 +467,8 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
         return
 
+    global SPLIT_CONV
+    SPLIT_CONV = args.split_conv
     plan = PLANS[args.workload](dev)
     stream = torch.cuda.current_stream()
     n_l = len(plan.launches)

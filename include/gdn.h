@@ -175,6 +175,27 @@ int gdn_postconv_l2(const void* y, int64_t y_row_stride, int in, int N,
                     int Hk, int Hv, int dk, int dv, float eps,
                     void* q_out, void* k_out, void* v_out, int out, void* stream);
 
+/* ---- 3b. conv and post-conv in one launch ---------------------------------
+ * gdn_causal_conv_fwd followed by gdn_postconv_l2 (out = act), with y kept
+ * on chip: each lane forms y for its 4 channels, rounds it to the
+ * activation dtype as the stored y would be, and applies SiLU, the head's
+ * sum of squares in the documented order (the post-conv's 16-lane tree,
+ * taken over the conv's 32 lanes per head) and the L2 scale on q and k.
+ * Results are bitwise equal to the two calls ("perf(gdn): optimize
+ * post-conv and causal-conv kernels", "What I verified": the fixed order is
+ * what makes that checkable).  conv_state is updated as by the conv.
+ *   x, x_row_stride, w, bias, conv_state, has_initial_state, cu_seqlens,
+ *   chunks, nchunks, nseq, N, write_state: as gdn_causal_conv_fwd
+ *   Hk, Hv, dk, dv, eps: as gdn_postconv_l2 (C = 2 Hk dk + Hv dv)
+ *   q, k (device) [N][Hk][dk] act; v (device) [N][Hv][dv] act; none may
+ *   overlap x, w, conv_state or each other (GDN_ERR_ALIAS). */
+int gdn_conv_postconv_fwd(const void* x, int64_t x_row_stride, int act,
+                          const float* w, const float* bias, float* conv_state,
+                          const uint8_t* has_initial_state, const int32_t* cu_seqlens,
+                          const gdn_chunk* chunks, int nchunks, int nseq, int N,
+                          int Hk, int Hv, int dk, int dv, float eps, int write_state,
+                          void* q, void* k, void* v, void* stream);
+
 /* ---- 4. chunked prefill --------------------------------------------------
  * Gated delta rule over every sequence of a varlen batch in chunks of 64
  * tokens (chunk-local K K^T and Q K^T on MFMA, unit-lower-triangular solve

@@ -155,6 +155,39 @@ int gdn_causal_conv_fwd(const void* x, int64_t xs, int act, const float* w, cons
                   "causal_conv");
 }
 
+int gdn_conv_postconv_fwd(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                          float* conv_state, const uint8_t* has_init, const int32_t* cu,
+                          const gdn_chunk* chunks, int nchunks, int nseq, int N, int Hk, int Hv, int dk,
+                          int dv, float eps, int write_state, void* q, void* k, void* v, void* stream) {
+  if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
+  int st = check_heads(Hk, Hv, dk, dv);
+  if (st != GDN_OK) return st;
+  const int C = 2 * Hk * dk + Hv * dv;
+  if (N < 0 || nseq < 0 || nchunks < 0 || xs < C)
+    return fail(GDN_ERR_SHAPE, "need N, nseq, nchunks >= 0 and x_row_stride >= C");
+  if (!(eps > 0.f)) return fail(GDN_ERR_SHAPE, "eps must be > 0");
+  if (N == 0 || nseq == 0 || nchunks == 0) return GDN_OK;
+  if (!x || !w || !conv_state || !cu || !chunks || !q || !k || !v)
+    return fail(GDN_ERR_NULL, "missing required pointer");
+  const int e = elem_bytes(act);
+  if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || !aligned16(conv_state) ||
+      (bias && !aligned16(bias)) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state, q, k and v must be 16-byte aligned");
+  const size_t nx = ((size_t)(N - 1) * xs + C) * e, ns = (size_t)nseq * 3 * C * 4;
+  const size_t nq = (size_t)N * Hk * dk * e, nv = (size_t)N * Hv * dv * e;
+  struct Buf { const void* p; size_t n; } out[4] = {{q, nq}, {k, nq}, {v, nv}, {conv_state, ns}};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(out[i].p, out[i].n, x, nx) || overlaps(out[i].p, out[i].n, w, (size_t)C * 16))
+      return fail(GDN_ERR_ALIAS, "q, k, v and conv_state must not overlap x, w or each other");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
+        return fail(GDN_ERR_ALIAS, "q, k, v and conv_state must not overlap x, w or each other");
+  }
+  return launched(gdn::launch_conv_postconv(x, xs, act, w, bias, conv_state, has_init, cu, chunks, nchunks,
+                                            Hk, Hv, eps, write_state, q, k, v, as_stream(stream)),
+                  "conv_postconv");
+}
+
 int gdn_postconv_l2(const void* y, int64_t ys, int in, int N, int Hk, int Hv, int dk, int dv,
                     float eps, void* q, void* k, void* v, int out, void* stream) {
   if (!valid_dtype(in) || !valid_dtype(out)) return fail(GDN_ERR_DTYPE, "unsupported dtype");

@@ -273,11 +273,179 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Conv and post-conv in one pass.  Each lane owns 8 adjacent channels (the
+// post-conv kernel's layout: a 128-channel head is one 16-lane DPP row, and
+// heads never straddle rows) and a wave takes kCPTokens consecutive tokens
+// of one chunk.  Per token the lane forms y for its channels as conv_kernel
+// does (same taps, same fused multiply-adds in the same order), rounds it
+// to the activation dtype as the stored y is rounded, and then runs the
+// post-conv kernel's lane function: SiLU, the head's squared norm in the
+// documented order, the L2 scale on q and k.  So q, k and v are bitwise
+// those of conv_kernel followed by postconv_kernel, and y never reaches
+// memory.  conv_state is read and written as in conv_kernel (wave 0 of a
+// sequence's first chunk, in place; its stored rows are read again at the
+// end for sequences shorter than 3 tokens, before they are overwritten).
+template <class T> struct CPShape;
+template <> struct CPShape<uint16_t> { static constexpr int kTok = 16; };   // 4 waves per chunk
+template <> struct CPShape<float> { static constexpr int kTok = 8; };       // 8 waves per chunk
+
+template <class T>
+__global__ __launch_bounds__(64 * 64 / CPShape<T>::kTok) void conv_post_kernel(
+    const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
+    float* conv_state, const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu,
+    const gdn_chunk* __restrict__ chunks, int C, int Hk, int Hv, float eps, int write_state,
+    T* __restrict__ q, T* __restrict__ k, T* __restrict__ v) {
+  constexpr int TPW = CPShape<T>::kTok;
+  using AT = Act<T>;
+  const gdn_chunk ch = chunks[blockIdx.x];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c0 = (blockIdx.y * 64 + lane) * 8;
+  if (ch.seq < 0 || c0 >= C) return;   // whole 16-lane rows: C is a multiple of 128
+  const int s = ch.seq;
+  const int t_begin = ch.begin + TPW * wave;
+  const int n = min(TPW, ch.end - t_begin);
+  const bool owner = wave == 0 && (ch.flags & GDN_CHUNK_FIRST) != 0;
+  if (n <= 0) return;
+
+  // taps and bias, then the window rows, then the token rows (one in-order
+  // counter: the first token waits only for what precedes it)
+  float w0[8], w1[8], w2[8], w3[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 wv = *reinterpret_cast<const float4*>(w + (int64_t)(c0 + i) * 4);
+    w0[i] = wv.x; w1[i] = wv.y; w2[i] = wv.z; w3[i] = wv.w;
+    b[i] = 0.f;
+  }
+  if (bias != nullptr) {
+    const float4 b0 = *reinterpret_cast<const float4*>(bias + c0);
+    const float4 b1 = *reinterpret_cast<const float4*>(bias + c0 + 4);
+    b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+  }
+  float h0[8], h1[8], h2[8];
+  float* st = conv_state + ((int64_t)s * 3) * C + c0;
+  const bool init = owner && seq_flag(has_init, s);
+  auto stored_row = [&](int r, float (&o)[8]) {
+    const float4 a = init ? *reinterpret_cast<const float4*>(st + (int64_t)r * C) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 c = init ? *reinterpret_cast<const float4*>(st + (int64_t)r * C + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = c.x; o[5] = c.y; o[6] = c.z; o[7] = c.w;
+  };
+  if (owner) {
+    stored_row(0, h0);
+    stored_row(1, h1);
+    stored_row(2, h2);
+  } else {
+    // the 3 rows before t_begin lie in the same sequence (a non-first chunk
+    // starts 64 tokens in or more, a later wave TPW w tokens in)
+    AT::load8(x + (int64_t)(t_begin - 3) * xs + c0, h0);
+    AT::load8(x + (int64_t)(t_begin - 2) * xs + c0, h1);
+    AT::load8(x + (int64_t)(t_begin - 1) * xs + c0, h2);
+  }
+  typename AT::Raw xr[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) xr[u] = AT::load_raw(x + (int64_t)(t_begin + min(u, n - 1)) * xs + c0);
+
+  // this lane's output row of token t_begin, and the row stride
+  const int qk = Hk * 128;
+  const bool is_qk = c0 < 2 * qk;
+  const int ors = is_qk ? qk : Hv * 128;
+  T* op = c0 < qk ? q + (int64_t)t_begin * qk + c0
+          : is_qk ? k + (int64_t)t_begin * qk + (c0 - qk)
+                  : v + (int64_t)t_begin * ors + (c0 - 2 * qk);
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    float xv[8], yv[8], sv[8];
+    AT::unpack(xr[u], xv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float acc = b[i];
+      acc = __builtin_fmaf(w0[i], h0[i], acc);
+      acc = __builtin_fmaf(w1[i], h1[i], acc);
+      acc = __builtin_fmaf(w2[i], h2[i], acc);
+      acc = __builtin_fmaf(w3[i], xv[i], acc);
+      h0[i] = h1[i]; h1[i] = h2[i]; h2[i] = xv[i];
+      yv[i] = acc;
+    }
+    // y as stored (rounded to the activation dtype, two at a time)
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const uint32_t pk = pack_bf16x2(yv[i], yv[i + 1]);
+        yv[i] = __uint_as_float(pk << 16);
+        yv[i + 1] = __uint_as_float(pk & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = silu<T>(yv[i]);
+    // every lane takes part in the row reduction (DPP needs its partners)
+    const float sum = head_sum_sq(sv);
+    if (u < n) {
+      if (is_qk) {
+        const float inv = 1.0f / __builtin_sqrtf(sum + eps);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sv[i] = sv[i] * inv;
+      }
+      AT::store8(op, sv);
+    }
+    op += ors;
+  }
+
+  if (owner && write_state) {
+    const int len = cu[s + 1] - cu[s];
+    const int eos = cu[s + 1];
+    // final rows r = 0..2 are xe[len-3+r]: x when that index is >= 0, else
+    // the stored row 3 + (len-3+r)
+    float r0[8], r1[8], r2[8];
+    if (len >= 3) {
+      AT::load8(x + (int64_t)(eos - 3) * xs + c0, r0);
+      AT::load8(x + (int64_t)(eos - 2) * xs + c0, r1);
+      AT::load8(x + (int64_t)(eos - 1) * xs + c0, r2);
+    } else {
+      float o1[8], o2[8], x0[8], x1[8];
+      stored_row(1, o1);
+      stored_row(2, o2);
+      AT::unpack(xr[0], x0);
+      AT::unpack(xr[1], x1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (len == 2) { r0[i] = o2[i]; r1[i] = x0[i]; r2[i] = x1[i]; }
+        else          { r0[i] = o1[i]; r1[i] = o2[i]; r2[i] = x0[i]; }   // len == 1
+      }
+    }
+    auto put = [&](int r, const float (&o)[8]) {
+      *reinterpret_cast<float4*>(st + (int64_t)r * C) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(st + (int64_t)r * C + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    };
+    put(0, r0);
+    put(1, r1);
+    put(2, r2);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out, int cap,
                               hipStream_t st) {
   hipLaunchKernelGGL(make_chunks_kernel, dim3(1), dim3(256), 0, st, cu, nseq, chunk_len, out, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_postconv(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                                float* conv_state, const uint8_t* has_init, const int32_t* cu,
+                                const gdn_chunk* chunks, int nchunks, int Hk, int Hv, float eps,
+                                int write_state, void* q, void* k, void* v, hipStream_t st) {
+  const int C = (2 * Hk + Hv) * 128;
+  dim3 grid(nchunks, (C + 511) / 512);
+  if (act == GDN_F32) {
+    hipLaunchKernelGGL(conv_post_kernel<float>, grid, dim3(64 * 64 / CPShape<float>::kTok), 0, st,
+                       static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks, C, Hk, Hv,
+                       eps, write_state, static_cast<float*>(q), static_cast<float*>(k), static_cast<float*>(v));
+  } else {
+    hipLaunchKernelGGL(conv_post_kernel<uint16_t>, grid, dim3(64 * 64 / CPShape<uint16_t>::kTok), 0, st,
+                       static_cast<const uint16_t*>(x), xs, w, bias, conv_state, has_init, cu, chunks, C, Hk,
+                       Hv, eps, write_state, static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
+                       static_cast<uint16_t*>(v));
+  }
   return hipGetLastError();
 }
 

@@ -17,6 +17,12 @@ hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const
                        float* conv_state, const uint8_t* has_init, const int32_t* cu,
                        const gdn_chunk* chunks, int nchunks, int C, int write_state, void* y,
                        hipStream_t st);
+// The conv with the post-conv step fused (q, k, v written instead of y;
+// bitwise equal to launch_conv followed by the post-conv with out = act).
+hipError_t launch_conv_postconv(const void* x, int64_t xs, int act, const float* w, const float* bias,
+                                float* conv_state, const uint8_t* has_init, const int32_t* cu,
+                                const gdn_chunk* chunks, int nchunks, int Hk, int Hv, float eps,
+                                int write_state, void* q, void* k, void* v, hipStream_t st);
 
 hipError_t launch_gates(const void* ba, int gate_act, const float* A_log, const float* dt_bias, int rows,
                         int Hv, float* g, float* beta, hipStream_t st);

@@ -73,6 +73,8 @@ _make_chunks = _sig("gdn_make_chunks", [_vp, _i32, _i32, _vp, _i32])
 _make_chunks_device = _sig("gdn_make_chunks_device", [_vp, _i32, _i32, _vp, _i32, _vp])
 _conv = _sig("gdn_causal_conv_fwd", [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                      _i32, _i32, _i32, _vp, _vp])
+_conv_post = _sig("gdn_conv_postconv_fwd", [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp])
 _postconv = _sig("gdn_postconv_l2", [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                                      _vp, _vp, _i32, _vp])
 _prefill = _sig("gdn_delta_rule_prefill", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
@@ -93,7 +95,7 @@ _out_norm = _sig("gdn_out_norm", [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _f32, _
 _gates = _sig("gdn_gates", [_vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp])
 
 EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
-            "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd",
+            "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd", "gdn_conv_postconv_fwd",
             "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_prefill_segmented_workspace",
             "gdn_delta_rule_prefill_segmented", "gdn_delta_rule_step", "gdn_commit",
             "gdn_decode_fused", "gdn_out_norm", "gdn_gates"]
@@ -210,6 +212,37 @@ def gdn_causal_conv_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.T
                  _ptr(has_initial_state), _ptr(cu_seqlens), _ptr(chunks), chunks.shape[0], nseq,
                  N, C, int(bool(write_state)), _ptr(y), _stream(stream)), "gdn_causal_conv_fwd")
     return y
+
+
+def gdn_conv_postconv_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor],
+                          conv_state: torch.Tensor, has_initial_state: Optional[torch.Tensor],
+                          cu_seqlens: torch.Tensor, chunks: torch.Tensor, write_state: bool,
+                          Hk: int, Hv: int, eps: float = 1e-6, q: Optional[torch.Tensor] = None,
+                          k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                          stream=None):
+    """Conv and post-conv in one launch (C ABI gdn_conv_postconv_fwd);
+    returns (q, k, v) in x's dtype, bitwise equal to gdn_causal_conv_fwd
+    followed by gdn_postconv_l2."""
+    N, C = x.shape
+    _require(x.stride(1) == 1, "x rows must be contiguous")
+    _require(C == (2 * Hk + Hv) * 128, "C must be (2 Hk + Hv) * 128")
+    nseq = cu_seqlens.numel() - 1
+    if q is None:
+        q = torch.empty(N, Hk, 128, dtype=x.dtype, device=x.device)
+    if k is None:
+        k = torch.empty(N, Hk, 128, dtype=x.dtype, device=x.device)
+    if v is None:
+        v = torch.empty(N, Hv, 128, dtype=x.dtype, device=x.device)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (w, "w"), (conv_state, "conv_state")):
+        _dense(t, nm)
+    _require(w.dtype == torch.float32 and conv_state.dtype == torch.float32, "w, conv_state: float32")
+    _require(bias is None or bias.dtype == torch.float32, "bias: float32")
+    _require(q.dtype == k.dtype == v.dtype == x.dtype, "q, k, v dtype must match x")
+    _check(_conv_post(_ptr(x), x.stride(0), _code(x.dtype), _ptr(w), _ptr(bias), _ptr(conv_state),
+                      _ptr(has_initial_state), _ptr(cu_seqlens), _ptr(chunks), chunks.shape[0], nseq, N,
+                      Hk, Hv, 128, 128, float(eps), int(bool(write_state)), _ptr(q), _ptr(k), _ptr(v),
+                      _stream(stream)), "gdn_conv_postconv_fwd")
+    return q, k, v
 
 
 # ---------------------------------------------------------------- post-conv

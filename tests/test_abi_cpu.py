@@ -206,6 +206,33 @@ def test_prefill_segmented_validation():
     assert call(ws=FAKE + (6 << 24) - 4096) == ALIAS   # workspace running into state
 
 
+def test_conv_postconv_validation():
+    fn = lib.gdn_conv_postconv_fwd
+    fn.restype = i32
+    fn.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                   vp, vp, vp, vp]
+    C = (2 * 2 + 4) * 128
+    base = [FAKE, C, 1, FAKE + (1 << 24), None, FAKE + (2 << 24), None, FAKE + (3 << 24), FAKE + (4 << 24),
+            3, 2, 100, 2, 4, 128, 128, 1e-6, 1, FAKE + (5 << 24), FAKE + (6 << 24), FAKE + (7 << 24), None]
+
+    def call(**kw):
+        a = list(base)
+        idx = {"xs": 1, "act": 2, "Hv": 13, "dk": 14, "eps": 16, "q": 18, "v": 20, "chunks": 8}
+        for k_, v_ in kw.items():
+            a[idx[k_]] = v_
+        return fn(*a)
+
+    assert call(Hv=3) == SHAPE
+    assert call(dk=64) == SHAPE
+    assert call(xs=C - 8) == SHAPE
+    assert call(eps=0.0) == SHAPE
+    assert call(act=5) == DTYPE
+    assert call(chunks=None) == NULL
+    assert call(q=FAKE + (5 << 24) + 8) == ALIGN
+    assert call(q=FAKE + 1024) == ALIAS                # q inside x
+    assert call(v=FAKE + (6 << 24) + 4096) == ALIAS    # v inside k
+
+
 def test_commit_validation():
     fn = lib.gdn_commit
     fn.restype = i32
