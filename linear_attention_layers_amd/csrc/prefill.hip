@@ -444,6 +444,7 @@ struct __attribute__((aligned(16))) SmemWS {
   uint16_t P[2][BT * LDT];
   float W[3][4][BT];          // per chunk: log2-scaled G, gamma, beta, d
   float Ad[4][16][20];        // diagonal block of A of each producer wave
+  uint16_t O[2][BT * 72];     // o of one chunk: 64 tokens x 64 state rows, rows padded to 144 B
   int len[kOrderMax];         // sequence lengths, for the longest-first order
   int pick;
 };
@@ -806,19 +807,35 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
             vr[b][ib][e] = __builtin_amdgcn_raw_buffer_load_b16(
                 rv, (((16 * ib + 4 * kg + e) * Hv + h) * DK + v0[b] + r16) * 2, 0, 0);
     };
-    // O of the previous chunk, packed, stored at the top of the next
-    // iteration: issued before that iteration's V loads, the stores are
-    // never inside a wait for loaded data (one in-order counter covers
-    // loads and stores)
+    // o leaves through LDS.  At the end of iteration c each wave writes its
+    // packed o (8 bytes per lane: 4 state rows of one token) into the
+    // staging buffer c & 1; after the barrier, at the top of iteration c+1,
+    // wave w stores tokens 16 w .. 16 w + 15 of all 64 rows as whole
+    // 128-byte row pieces (16 bytes per lane, two stores).  Direct stores
+    // from the accumulator layout wrote 32-byte pieces, 16 tokens apart per
+    // instruction, four per wave and chunk, and cost about a sixth of the
+    // kernel time.  The stores are issued after the next chunk's V loads:
+    // one in-order counter covers loads and stores, so the wait for those
+    // loads never includes them.  Buffer c & 1 is written again only after
+    // the barrier that ends iteration c+1, when every wave has stored it.
+    // The row padding (16 bytes) makes the 8-byte writes free of bank
+    // conflicts (16 tokens x 2 granules per half wave); the two 16-byte
+    // reads per chunk overlap on 4 of the 64 banks.
+    static_assert(VB == 1, "the o staging buffer holds 64 state rows");
     u32x2 opk[VB][4];
     __amdgpu_buffer_rsrc_t ro_prev = buf_rsrc(o, 0);
-    auto store_o = [&]() {
+    auto stage_o = [&](int buf) {
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
+        *reinterpret_cast<u32x2*>(&sm.O[buf][(16 * ib + r16) * 72 + 16 * w + 4 * kg]) = opk[0][ib];
+    };
+    auto store_o = [&](int buf) {
 #pragma unroll
-        for (int b = 0; b < VB; ++b)
-          __builtin_amdgcn_raw_buffer_store_b64(opk[b][ib], ro_prev,
-                                                (((16 * ib + r16) * Hv + h) * DK + v0[b] + 4 * kg) * 2, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const int tok = 16 * w + 8 * j + (lane >> 3), gq = lane & 7;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.O[buf][tok * 72 + 8 * gq]);
+        __builtin_amdgcn_raw_buffer_store_b128(val, ro_prev, ((tok * Hv + h) * DK + slice * DVS + 8 * gq) * 2, 0, 0);
+      }
     };
 #pragma unroll
     for (int b = 0; b < VB; ++b)
@@ -846,14 +863,15 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
           for (int e = 0; e < 4; ++e) vv[b][ib][e] = bf16_to_f32(vr[b][ib][e]);
-      if (WO) store_o();
       load_v(c + 1);
+      if (WO && c > 0) store_o((c - 1) & 1);
 
       // The chain of the chunk is Z -> R -> the four block steps of the
       // solve -> the state update.  Each U block, once final, immediately
-      // feeds its share of the state update and of O, and the Q S0^T
-      // products are spread between the block steps, so the MFMA pipe has
-      // independent work while a block step waits on its predecessor.
+      // feeds its share of the state update and of O.  The Q S0^T products
+      // are formed before the solve: between the block steps their fragment
+      // reads queued ahead of each step's own LDS reads (LDS returns in
+      // order) and lengthened the chain.
       // S0 is read as bf16 operands taken before the update (sb), so the
       // float32 state is updated in place.
 
@@ -946,13 +964,18 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       // between the two shapes that the compiler does not insert (the
       // second one read stale accumulator elements), so mixed-shape sums are
       // formed on separate accumulators and added.
+      if (WO) {
+        qs_step(0);
+        qs_step(1);
+        qs_step(2);
+        qs_step(3);
+      }
       f32x4 uu[VB][4], pu[VB][4];
       {
         const auto td = PR::lds16(ATc, LDT, r16, 0, kg);
 #pragma unroll
         for (int b = 0; b < VB; ++b) uu[b][0] = PR::mma16(td, PR::reg16(rr[b][0]), zero4());
       }
-      if (WO) qs_step(0);
       {
         const auto am = PR::lds16(ATc, LDT, 16 + r16, 0, kg);
         const auto td = PR::lds16(ATc, LDT, 16 + r16, 16, kg);
@@ -962,7 +985,6 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           uu[b][1] = PR::mma16(td, PR::reg16(rr[b][1]), zero4());
         }
       }
-      if (WO) qs_step(1);
       {
         // blocks 0 and 1 are final: first half of the state update and
         // their part of O
@@ -1003,7 +1025,6 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
 #pragma unroll
         for (int b = 0; b < VB; ++b) uu[b][2] = PR::mma16(td, PR::reg16(rr[b][2]), zero4());
       }
-      if (WO) qs_step(2);
       {
         const auto am = PR::lds16(ATc, LDT, 48 + r16, 32, kg);
         const auto td = PR::lds16(ATc, LDT, 48 + r16, 48, kg);
@@ -1015,7 +1036,6 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           uu[b][3] = PR::mma16(td, PR::reg16(rr[b][3]), zero4());
         }
       }
-      if (WO) qs_step(3);
       {
         // blocks 2 and 3: second half of the state update and the rest of O
         typename PR::F32 du[VB], u23[VB];
@@ -1059,10 +1079,11 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
             opk[b][ib] = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
           }
         }
+        stage_o(c & 1);
       }
       __syncthreads();
     }
-    if (WO) store_o();
+    if (WO) store_o((nc - 1) & 1);
   }
 
   if (dst != nullptr) {
