@@ -444,7 +444,7 @@ struct __attribute__((aligned(16))) SmemWS {
   uint16_t P[2][BT * LDT];
   float W[3][4][BT];          // per chunk: log2-scaled G, gamma, beta, d
   float Ad[4][16][20];        // diagonal block of A of each producer wave
-  uint16_t O[2][BT * 72];     // o of one chunk: 64 tokens x 64 state rows, rows padded to 144 B
+  uint16_t O[2][BT * 72];     // V / o staging: 64 tokens x 64 state rows, rows padded to 144 B
   int len[kOrderMax];         // sequence lengths, for the longest-first order
   int pick;
 };
@@ -792,36 +792,53 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     // a compile-time constant except in the first segment pass, where it is
     // uniform over the workgroup
     const bool WO = o_on_wg;
-    // V of one chunk in the accumulator layout: lane holds tokens
-    // 16 ib + 4 kg + e of state row v0 + r16
-    uint16_t vr[VB][4][4];
+    // V enters and o leaves through two LDS tiles X[0], X[1] of 64 tokens x
+    // 64 state rows (bf16, rows padded to 144 bytes).  Global memory sees
+    // whole 128-byte row pieces only: wave w moves tokens 16 w .. 16 w + 15
+    // of all 64 rows, 16 bytes per lane, two accesses per chunk.  The MFMA
+    // side works on the wave's own 16 state rows of all tokens.  In
+    // iteration c:
+    //   top: read V(c) from X[c & 1] (own rows, transposing reads into the
+    //        accumulator layout); read o(c-1) from X[(c+1) & 1] (own
+    //        tokens), then write V(c+1), loaded one iteration earlier, into
+    //        the same place; issue the loads of V(c+2), then the stores of
+    //        o(c-1);
+    //   end: write o(c) into X[c & 1] (own rows, where V(c) was read).
+    // So within an iteration a wave touches X[c & 1] only in its own rows
+    // and X[(c+1) & 1] only in its own tokens; what another wave wrote is
+    // read only after the barrier that ends the iteration.  The stores come
+    // after the V loads: one in-order counter covers loads and stores, so
+    // the wait for those loads never includes a store.  Direct global
+    // accesses in the accumulator layout moved 32-byte pieces (16 loads of
+    // 2 bytes and 4 stores of 8 bytes per lane and chunk) and cost about a
+    // fifth of the kernel time.  The row padding makes the 8-byte o writes
+    // free of bank conflicts within a half wave.
+    static_assert(VB == 1, "the V / o staging tiles hold 64 state rows");
+    const int tok_w = 16 * w + (lane >> 3), gq = lane & 7;   // token-side piece: + 8 j
+    u32x4 vg[2];
     auto load_v = [&](int c) {
       const int64_t c0 = bos + BT * c;
       const auto rv = buf_rsrc(v + c0 * Hv * DK, v_on ? chunk_len(c) * Hv * DK * 2 : 0);
 #pragma unroll
-      for (int b = 0; b < VB; ++b)
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            vr[b][ib][e] = __builtin_amdgcn_raw_buffer_load_b16(
-                rv, (((16 * ib + 4 * kg + e) * Hv + h) * DK + v0[b] + r16) * 2, 0, 0);
+      for (int j = 0; j < 2; ++j)
+        vg[j] = __builtin_amdgcn_raw_buffer_load_b128(rv, (((tok_w + 8 * j) * Hv + h) * DK + slice * DVS + 8 * gq) * 2, 0, 0);
     };
-    // o leaves through LDS.  At the end of iteration c each wave writes its
-    // packed o (8 bytes per lane: 4 state rows of one token) into the
-    // staging buffer c & 1; after the barrier, at the top of iteration c+1,
-    // wave w stores tokens 16 w .. 16 w + 15 of all 64 rows as whole
-    // 128-byte row pieces (16 bytes per lane, two stores).  Direct stores
-    // from the accumulator layout wrote 32-byte pieces, 16 tokens apart per
-    // instruction, four per wave and chunk, and cost about a sixth of the
-    // kernel time.  The stores are issued after the next chunk's V loads:
-    // one in-order counter covers loads and stores, so the wait for those
-    // loads never includes them.  Buffer c & 1 is written again only after
-    // the barrier that ends iteration c+1, when every wave has stored it.
-    // The row padding (16 bytes) makes the 8-byte writes free of bank
-    // conflicts (16 tokens x 2 granules per half wave); the two 16-byte
-    // reads per chunk overlap on 4 of the 64 banks.
-    static_assert(VB == 1, "the o staging buffer holds 64 state rows");
+    auto put_v = [&](int buf) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&sm.O[buf][(tok_w + 8 * j) * 72 + 8 * gq]) = vg[j];
+    };
+    // V(c) of this lane: tokens 16 ib + 4 kg + e of state row 16 w + r16
+    // (ds_read_b64_tr_b16: result lane i, slot j comes from source lane
+    // 4 j + i / 4, slot i % 4, within each 16-lane group)
+    auto get_v = [&](int buf, float (&vv)[4][4]) {
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(&sm.O[buf][(16 * ib + 4 * kg + (r16 >> 2)) * 72 + 4 * (4 * w + (r16 & 3))]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[ib][e] = bf16_to_f32(static_cast<uint16_t>(x[e]));
+      }
+    };
     u32x2 opk[VB][4];
     __amdgpu_buffer_rsrc_t ro_prev = buf_rsrc(o, 0);
     auto stage_o = [&](int buf) {
@@ -829,19 +846,23 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       for (int ib = 0; ib < 4; ++ib)
         *reinterpret_cast<u32x2*>(&sm.O[buf][(16 * ib + r16) * 72 + 16 * w + 4 * kg]) = opk[0][ib];
     };
-    auto store_o = [&](int buf) {
+    u32x4 og[2];
+    auto read_o = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int tok = 16 * w + 8 * j + (lane >> 3), gq = lane & 7;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.O[buf][tok * 72 + 8 * gq]);
-        __builtin_amdgcn_raw_buffer_store_b128(val, ro_prev, ((tok * Hv + h) * DK + slice * DVS + 8 * gq) * 2, 0, 0);
-      }
+      for (int j = 0; j < 2; ++j) og[j] = *reinterpret_cast<const u32x4*>(&sm.O[buf][(tok_w + 8 * j) * 72 + 8 * gq]);
+    };
+    auto store_o = [&]() {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(og[j], ro_prev, (((tok_w + 8 * j) * Hv + h) * DK + slice * DVS + 8 * gq) * 2, 0, 0);
     };
 #pragma unroll
     for (int b = 0; b < VB; ++b)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) opk[b][ib] = u32x2{0u, 0u};
     load_v(0);
+    put_v(0);
+    load_v(1);
     __syncthreads();
     __syncthreads();
 
@@ -857,14 +878,11 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       const float gamma_last = __builtin_amdgcn_exp2f(Wc[n - 1]);
 
       float vv[VB][4][4];
-#pragma unroll
-      for (int b = 0; b < VB; ++b)
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv[b][ib][e] = bf16_to_f32(vr[b][ib][e]);
-      load_v(c + 1);
-      if (WO && c > 0) store_o((c - 1) & 1);
+      get_v(c & 1, vv[0]);
+      if (WO && c > 0) read_o((c + 1) & 1);
+      put_v((c + 1) & 1);
+      load_v(c + 2);
+      if (WO && c > 0) store_o();
 
       // The chain of the chunk is Z -> R -> the four block steps of the
       // solve -> the state update.  Each U block, once final, immediately
@@ -1083,7 +1101,10 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       }
       __syncthreads();
     }
-    if (WO) store_o((nc - 1) & 1);
+    if (WO) {
+      read_o((nc - 1) & 1);
+      store_o();
+    }
   }
 
   if (dst != nullptr) {
