@@ -164,9 +164,10 @@ int gdn_causal_conv_fwd(const void* x, int64_t x_row_stride, int act,
  * ("What I verified", "The one thing I changed in your tests".)
  * The squared norm is summed in one fixed order: a pairwise tree,
  * neighbours first (level l adds adjacent blocks of 2^l elements), each
- * step one float32 addition with no fused multiply-add; float32 sqrt and
- * division are correctly rounded.  For a float32 output, SiLU is evaluated
- * in float64 and rounded once to float32.
+ * step one float32 addition with no fused multiply-add.  For a float32
+ * output, sqrt and division are correctly rounded and SiLU is evaluated in
+ * float64 and rounded once to float32; for a bf16 output the scale is the
+ * hardware reciprocal square root (about one float32 ulp).
  *   y      (device) [N][y_row_stride] act `in`, y_row_stride >= C
  *   q_out, k_out (device) [N][Hk][dk], v_out [N][Hv][dv], dtype `out`;
  *          none may overlap y

@@ -381,7 +381,7 @@ __global__ __launch_bounds__(64 * 64 / CPShape<T>::kTok) void conv_post_kernel(
     const float sum = head_sum_sq(sv);
     if (u < n) {
       if (is_qk) {
-        const float inv = 1.0f / __builtin_sqrtf(sum + eps);
+        const float inv = l2_inv<T>(sum, eps);
 #pragma unroll
         for (int i = 0; i < 8; ++i) sv[i] = sv[i] * inv;
       }

@@ -151,6 +151,20 @@ template <> __device__ __forceinline__ float silu<uint16_t>(float y) {
   return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// 1 / sqrt(sum + eps), the L2 scale of a q or k head.  A float32 output
+// carries the correctly rounded square root and division.  A bf16 output
+// takes the hardware reciprocal square root (about one float32 ulp, a
+// single transcendental instead of the two correction sequences), whose
+// error is far below a bf16 step; the argument is kept at or above the
+// smallest normal float32.
+template <class TO> __device__ __forceinline__ float l2_inv(float sum, float eps);
+template <> __device__ __forceinline__ float l2_inv<float>(float sum, float eps) {
+  return 1.0f / __builtin_sqrtf(sum + eps);
+}
+template <> __device__ __forceinline__ float l2_inv<uint16_t>(float sum, float eps) {
+  return __builtin_amdgcn_rsqf(__builtin_fmaxf(sum + eps, 1.17549435e-38f));
+}
+
 __device__ __forceinline__ float head_sum_sq(const float (&s)[8]) {
 #pragma clang fp contract(off)
   const float p0 = s[0] * s[0] + s[1] * s[1];
@@ -170,7 +184,7 @@ __device__ __forceinline__ void postconv_lane(const float (&raw)[8], bool is_qk,
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = silu<TO>(raw[i]);
   const float sum = head_sum_sq(s);
-  const float inv = 1.0f / __builtin_sqrtf(sum + eps);
+  const float inv = l2_inv<TO>(sum, eps);
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = is_qk ? s[i] * inv : s[i];
 }

@@ -14,8 +14,9 @@
 // neighbours-first tree ((e0+e1)+(e2+e3))+((e4+e5)+(e6+e7)); the 16 lane
 // partials are then combined by xor-1, xor-2, xor-4, xor-8 DPP butterflies.
 // Together this is the pairwise tree over the 128 elements in which level l
-// adds adjacent blocks of 2^l elements.  inv = 1/sqrt(sum + eps) with
-// correctly rounded sqrt and division; q_hat = s * inv.
+// adds adjacent blocks of 2^l elements.  inv = 1/sqrt(sum + eps), with
+// correctly rounded sqrt and division for a float32 output and the hardware
+// reciprocal square root for a bf16 output; q_hat = s * inv.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(kPostThreads) void postconv_kernel(
     const float sum = head_sum_sq(s);
     if (!active || t >= N) continue;
     if (c0 < 2 * qk) {
-      const float inv = 1.0f / __builtin_sqrtf(sum + eps);
+      const float inv = l2_inv<TO>(sum, eps);
       float out[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) out[i] = s[i] * inv;
