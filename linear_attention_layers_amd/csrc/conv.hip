@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     const gdn_chunk* __restrict__ chunks, int C, int write_state, T* __restrict__ y) {
   using A = Act4<T>;
   const gdn_chunk ch = chunks[blockIdx.x];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c0 = (blockIdx.y * 64 + lane) * kConvChannelsPerLane;
   if (ch.seq < 0 || c0 >= C) return;
   const int s = ch.seq;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64 * 64 / CPShape<T>::kTok) void conv_post_kernel(
   constexpr int TPW = CPShape<T>::kTok;
   using AT = Act<T>;
   const gdn_chunk ch = chunks[blockIdx.x];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   if (ch.seq < 0 || c0 >= C) return;   // whole 16-lane rows: C is a multiple of 128
   const int s = ch.seq;
