@@ -11,7 +11,10 @@ starts.
 
 Prints ONE JSON line: throughput in tokens/s, the roofline of the dominant
 kernel (per-launch HIP-event time of each kernel inside the timed region),
-and the CPU oracle timed on a bounded sample of the same workload.
+the CPU oracle timed on a bounded sample of the same workload, and a
+cold-cache pass (`cold_cache`: up to 20 more steps, each after a 1 GiB read
+that evicts L2 and the Infinity Cache, timed with events; context beside
+`value`, which is the warm timed region).
 
 Other workloads (--workload), each one JSON line with per-kernel stages and
 the dominant kernel's roofline, throughput in layer-tokens/s:
@@ -429,6 +432,39 @@ PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed
          "gates": plan_gates, "long-seg": lambda dev: plan_long(dev, nseg=4)}
 
 
+def cold_pass(plan, stream, reps):
+    """Each of `reps` steps runs right after a 1 GiB read of an unrelated
+    buffer (clean lines: it evicts L2 and the Infinity Cache without leaving
+    write-backs behind), with HIP events on the launch stream around every
+    kernel and around the step; the read itself is outside the events."""
+    import torch
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=stream.device)
+    names = list(dict.fromkeys(nm for nm, _ in plan.launches))
+    acc = {nm: 0.0 for nm in names}
+    total = 0.0
+    for _ in range(reps):
+        scratch.sum()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan.launches) + 1)]
+        ev[0].record(stream)
+        for i, (_, fn) in enumerate(plan.launches):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for j, (nm, _) in enumerate(plan.launches):
+            acc[nm] += ev[j].elapsed_time(ev[j + 1])
+        total += ev[0].elapsed_time(ev[-1])
+    del scratch
+    stages = {}
+    for nm in names:
+        rec = {"us_per_launch": round(acc[nm] / reps * 1e3 / plan.count[nm], 2)}
+        if plan.bytes.get(nm):
+            rec["hbm_frac"] = round(plan.bytes[nm] / (acc[nm] / reps / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+        stages[nm] = rec
+    ms = total / reps
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(plan.tokens / (ms / 1e3), 1),
+            "steps": reps, "flush_bytes": 1 << 30, "stages": stages}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -436,6 +472,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", choices=sorted(PLANS), default="varlen")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache pass (steps run after a 1 GiB read that evicts L2 and the "
+                         "256 MB Infinity Cache; reported beside the timed region, never as value)")
     ap.add_argument("--split-conv", action="store_true",
                     help="run the conv and the post-conv as two launches instead of the fused one")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -550,6 +589,8 @@ def main():
                      "algorithmic_bytes": plan.bytes[dominant] // plan.count[dominant]},
         "stages": stages,
     }
+    if not args.no_cold:
+        out["cold_cache"] = cold_pass(plan, stream, min(steps, 20))
     if args.workload == "varlen" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(plan.lb)
     print(json.dumps(out), flush=True)
