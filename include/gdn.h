@@ -5,7 +5,9 @@
  *   1. exact token chunks for the conv          gdn_make_chunks / _device
  *   2. width-4 depthwise causal conv             gdn_causal_conv_fwd
  *   3. SiLU + q|k|v split + per-head L2 norm     gdn_postconv_l2
+ *      2 and 3 in one launch                     gdn_conv_postconv_fwd
  *   4. chunked gated delta-rule prefill          gdn_delta_rule_prefill
+ *      segment-parallel form for long sequences  gdn_delta_rule_prefill_segmented
  *   5. per-token decode / verify step            gdn_delta_rule_step
  *   6. layer-batched commit of a verify window   gdn_commit
  *   7. fused decode / verify: conv + post-conv + step in one launch
@@ -28,8 +30,9 @@
  *
  * Conventions shared by every call
  *   - Pointers marked (device) are device memory; (host) is host memory.
- *     The caller owns every buffer.  The library allocates nothing, keeps no
- *     state between calls and is safe to call from several host threads.
+ *     The caller owns every buffer.  The library allocates nothing (the
+ *     segmented prefill takes a caller-owned workspace), keeps no state
+ *     between calls and is safe to call from several host threads.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  A returned GDN_OK means the launch was accepted.
  *   - Activations are float32 (GDN_F32) or bfloat16 (GDN_BF16); conv weights,
