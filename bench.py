@@ -1,9 +1,11 @@
 """GDN layer hot-path benchmark on one MI355X.
 
 Default workload (the headline metric): the bf16 varlen prefill.  One step
-is one pass of the whole hot path over one batch: exact conv chunks (device
-builder), causal conv with the conv_state update, post-conv (SiLU, split,
-L2) and the chunked delta-rule prefill with the state update, on 8
+is one pass of the whole hot path over one batch: exact 64-token conv chunks
+(derived from cu_seqlens inside the conv launch; --chunk-descriptors runs
+the descriptor builder instead), causal conv with the conv_state update and
+post-conv (SiLU, split, L2) in one launch, and the chunked delta-rule
+prefill with the state update, on 8
 sequences with lengths uniform in [128, 2048], 8192 packed channels = 16 q
 + 16 k heads and 32 v heads of 128, half of the sequences with initial
 states.  Inputs are synthetic and seeded, resident in HBM before timing
@@ -89,8 +91,15 @@ def postconv_bytes(N, C, e):
 
 # The conv and the post-conv run as one launch (gdn_conv_postconv_fwd) unless
 # --split-conv asks for the two separate launches.  The fused launch moves
-# conv_bytes: x in, q|k|v (N x C) out instead of y.
+# conv_bytes: x in, q|k|v (N x C) out instead of y.  It derives the 64-token
+# chunks from cu_seqlens itself unless --chunk-descriptors (or --split-conv,
+# whose conv needs them) asks for the descriptor builder's launch.
 SPLIT_CONV = False
+CHUNK_DESCRIPTORS = False
+
+
+def descriptors_needed() -> bool:
+    return SPLIT_CONV or CHUNK_DESCRIPTORS
 
 
 def add_conv_post(p, x, w, cs, hi, cu, chunks, write_state, Hk, Hv, N, C, n_init, nseq, y, q, k, v):
@@ -232,8 +241,10 @@ def plan_varlen(dev):
     chunks = torch.empty(gdn.gdn_chunk_capacity(N, lb.nseq), 4, dtype=torch.int32, device=dev)
     algo = algorithmic_bytes(lb)
     p = Plan()
-    p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
-    add_conv_post(p, d["x"], d["w"], d["cs"], d["hi"], d["cu"], chunks, True, Hk, Hv, N, lb.geo.C,
+    if descriptors_needed():
+        p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
+    add_conv_post(p, d["x"], d["w"], d["cs"], d["hi"], d["cu"], chunks if descriptors_needed() else None,
+                  True, Hk, Hv, N, lb.geo.C,
                   int(lb.has_init.sum()), lb.nseq, d["y"], d["q"], d["k"], d["v"])
     p.add("prefill", lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                         d["cu"], d["st"], d["hi"], o=d["o"]),
@@ -270,7 +281,8 @@ def plan_verify(dev, fused=False):
                       v_out=d["v"]),
                   fused_bytes(N, C, Hk, Hv, 2, lb.nseq, False, 0, True))
         else:
-            add_conv_post(p, d["x"], d["w"], d["cs"], None, d["cu"], d["chunks"], False, Hk, Hv, N, C,
+            add_conv_post(p, d["x"], d["w"], d["cs"], None, d["cu"], d["chunks"] if descriptors_needed() else None,
+                          False, Hk, Hv, N, C,
                           lb.nseq, lb.nseq, d["y"], d["q"], d["k"], d["v"])
             p.add("step", lambda d=d: gdn.gdn_delta_rule_step(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                                               d["cu"], d["st"], None, o=d["o"],
@@ -302,8 +314,10 @@ def plan_long(dev, nseg=1):
     Hk, Hv, N, C = lb.geo.Hk, lb.geo.Hv, lb.N, lb.geo.C
     chunks = torch.empty(gdn.gdn_chunk_capacity(N, lb.nseq), 4, dtype=torch.int32, device=dev)
     p = Plan()
-    p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
-    add_conv_post(p, d["x"], d["w"], d["cs"], d["hi"], d["cu"], chunks, True, Hk, Hv, N, C, 0, 1, d["y"],
+    if descriptors_needed():
+        p.add("chunks", lambda: gdn.gdn_make_chunks_device(d["cu"], N, out=chunks), 0)
+    add_conv_post(p, d["x"], d["w"], d["cs"], d["hi"], d["cu"], chunks if descriptors_needed() else None,
+                  True, Hk, Hv, N, C, 0, 1, d["y"],
                   d["q"], d["k"], d["v"])
     if nseg == 1:
         run = lambda: gdn.gdn_delta_rule_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"],
@@ -345,11 +359,13 @@ def plan_mixed(dev, fused=False):
             # conv and post-conv over the prefill tokens only; the decode
             # tokens go through the fused launch
             d["chunks_pre"] = gdn.gdn_make_chunks_device(d["cu_pre"], Npre)
-            add_conv_post(p, d["x"][:Npre], d["w"], d["cs"][:npre], None, d["cu_pre"], d["chunks_pre"], True,
+            add_conv_post(p, d["x"][:Npre], d["w"], d["cs"][:npre], None, d["cu_pre"],
+                          d["chunks_pre"] if descriptors_needed() else None, True,
                           Hk, Hv, Npre, C, npre, npre, d["y"][:Npre], d["q"][:Npre], d["k"][:Npre],
                           d["v"][:Npre])
         else:
-            add_conv_post(p, d["x"], d["w"], d["cs"], None, d["cu"], d["chunks"], True, Hk, Hv, N, C,
+            add_conv_post(p, d["x"], d["w"], d["cs"], None, d["cu"], d["chunks"] if descriptors_needed() else None,
+                          True, Hk, Hv, N, C,
                           lb.nseq, lb.nseq, d["y"], d["q"], d["k"], d["v"])
         p.add("prefill", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_prefill(
                   d["q"][:n], d["k"][:n], d["v"][:n], d["g"][:n], d["beta"][:n], d["cu_pre"],
@@ -475,6 +491,9 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (steps run after a 1 GiB read that evicts L2 and the "
                          "256 MB Infinity Cache; reported beside the timed region, never as value)")
+    ap.add_argument("--chunk-descriptors", action="store_true",
+                    help="build the conv chunk descriptors in their own launch (gdn_make_chunks_device) "
+                         "instead of deriving them inside the conv launch")
     ap.add_argument("--split-conv", action="store_true",
                     help="run the conv and the post-conv as two launches instead of the fused one")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -506,8 +525,9 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": 5}), flush=True)
         return
 
-    global SPLIT_CONV
+    global SPLIT_CONV, CHUNK_DESCRIPTORS
     SPLIT_CONV = args.split_conv
+    CHUNK_DESCRIPTORS = args.chunk_descriptors
     plan = PLANS[args.workload](dev)
     stream = torch.cuda.current_stream()
     n_l = len(plan.launches)

@@ -189,7 +189,11 @@ int gdn_postconv_l2(const void* y, int64_t y_row_stride, int in, int N,
  * post-conv and causal-conv kernels", "What I verified": the fixed order is
  * what makes that checkable).  conv_state is updated as by the conv.
  *   x, x_row_stride, w, bias, conv_state, has_initial_state, cu_seqlens,
- *   chunks, nchunks, nseq, N, write_state: as gdn_causal_conv_fwd
+ *   chunks, nchunks, nseq, N, write_state: as gdn_causal_conv_fwd, except
+ *   that chunks may be NULL when nseq <= 64: the launch then derives the
+ *   64-token chunks of gdn_make_chunks from cu_seqlens itself (nchunks is
+ *   not used; the same chunks, so the same results), saving the
+ *   descriptor-builder launch.  NULL with nseq > 64 is GDN_ERR_SHAPE.
  *   Hk, Hv, dk, dv, eps: as gdn_postconv_l2 (C = 2 Hk dk + Hv dv)
  *   q, k (device) [N][Hk][dk] act; v (device) [N][Hv][dv] act; none may
  *   overlap x, w, conv_state or each other (GDN_ERR_ALIAS). */

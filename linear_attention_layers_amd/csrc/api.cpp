@@ -166,8 +166,14 @@ int gdn_conv_postconv_fwd(const void* x, int64_t xs, int act, const float* w, co
   if (N < 0 || nseq < 0 || nchunks < 0 || xs < C)
     return fail(GDN_ERR_SHAPE, "need N, nseq, nchunks >= 0 and x_row_stride >= C");
   if (!(eps > 0.f)) return fail(GDN_ERR_SHAPE, "eps must be > 0");
+  // chunks == NULL: the launch derives the 64-token chunks from cu_seqlens
+  // (nseq <= 64), over floor(N / 64) + nseq slots; nchunks is not used
+  if (chunks == nullptr) {
+    if (nseq > 64) return fail(GDN_ERR_SHAPE, "chunks may be NULL only for nseq <= 64 (got %d)", nseq);
+    nchunks = N / 64 + nseq;
+  }
   if (N == 0 || nseq == 0 || nchunks == 0) return GDN_OK;
-  if (!x || !w || !conv_state || !cu || !chunks || !q || !k || !v)
+  if (!x || !w || !conv_state || !cu || !q || !k || !v)
     return fail(GDN_ERR_NULL, "missing required pointer");
   const int e = elem_bytes(act);
   if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || !aligned16(conv_state) ||
@@ -183,7 +189,7 @@ int gdn_conv_postconv_fwd(const void* x, int64_t xs, int act, const float* w, co
       if (overlaps(out[i].p, out[i].n, out[j].p, out[j].n))
         return fail(GDN_ERR_ALIAS, "q, k, v and conv_state must not overlap x, w or each other");
   }
-  return launched(gdn::launch_conv_postconv(x, xs, act, w, bias, conv_state, has_init, cu, chunks, nchunks,
+  return launched(gdn::launch_conv_postconv(x, xs, act, w, bias, conv_state, has_init, cu, chunks, nchunks, nseq,
                                             Hk, Hv, eps, write_state, q, k, v, as_stream(stream)),
                   "conv_postconv");
 }

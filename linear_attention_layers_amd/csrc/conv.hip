@@ -290,16 +290,42 @@ template <class T> struct CPShape;
 template <> struct CPShape<uint16_t> { static constexpr int kTok = 16; };   // 4 waves per chunk
 template <> struct CPShape<float> { static constexpr int kTok = 8; };       // 8 waves per chunk
 
+// The 64-token chunk of slot j, derived from cu_seqlens (nseq <= 64) when no
+// descriptor list is given.  f(s) = floor(cu[s] / 64) + s is strictly
+// increasing (f(s+1) - f(s) = floor(cu[s+1]/64) - floor(cu[s]/64) + 1 >= 1),
+// and sequence s owns slots f(s) .. f(s) + ceil(L_s / 64) - 1, which stay
+// below f(s+1): floor(a/64) + ceil(L/64) <= floor((a+L)/64) + 1.  So slot j
+// belongs to the last s with f(s) <= j (a prefix of the lanes, counted by a
+// ballot), as chunk c = j - f(s) if c < ceil(L_s / 64); otherwise the slot
+// is empty (seq = -1).  Slots number floor(N / 64) + nseq.  The chunks and
+// their order within a sequence are those of the descriptor builder.
+__device__ __forceinline__ gdn_chunk derive_chunk(const int32_t* __restrict__ cu, int nseq, int j, int lane) {
+  const int b = lane < nseq ? cu[lane] : 0;
+  const int e = lane < nseq ? cu[lane + 1] : 0;
+  const int f = (b >> 6) + lane;
+  const uint64_t below = __builtin_amdgcn_ballot_w64(lane < nseq && f <= j);
+  const int s = __builtin_popcountll(below) - 1;   // f(0) = 0 <= j: s >= 0
+  const int bs = __builtin_amdgcn_readlane(b, s), es = __builtin_amdgcn_readlane(e, s);
+  const int c = j - __builtin_amdgcn_readlane(f, s);
+  const int nc = (es - bs + 63) >> 6;
+  gdn_chunk ch;
+  ch.seq = c < nc ? s : -1;
+  ch.begin = bs + 64 * c;
+  ch.end = min(ch.begin + 64, es);
+  ch.flags = (c == 0 ? GDN_CHUNK_FIRST : 0) | (c == nc - 1 ? GDN_CHUNK_LAST : 0);
+  return ch;
+}
+
 template <class T>
 __global__ __launch_bounds__(64 * 64 / CPShape<T>::kTok) void conv_post_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
     float* conv_state, const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu,
-    const gdn_chunk* __restrict__ chunks, int C, int Hk, int Hv, float eps, int write_state,
+    const gdn_chunk* __restrict__ chunks, int nseq, int C, int Hk, int Hv, float eps, int write_state,
     T* __restrict__ q, T* __restrict__ k, T* __restrict__ v) {
   constexpr int TPW = CPShape<T>::kTok;
   using AT = Act<T>;
-  const gdn_chunk ch = chunks[blockIdx.x];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const gdn_chunk ch = chunks != nullptr ? chunks[blockIdx.x] : derive_chunk(cu, nseq, blockIdx.x, lane);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
   if (ch.seq < 0 || c0 >= C) return;   // whole 16-lane rows: C is a multiple of 128
   const int s = ch.seq;
@@ -432,18 +458,18 @@ hipError_t launch_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_ch
 
 hipError_t launch_conv_postconv(const void* x, int64_t xs, int act, const float* w, const float* bias,
                                 float* conv_state, const uint8_t* has_init, const int32_t* cu,
-                                const gdn_chunk* chunks, int nchunks, int Hk, int Hv, float eps,
+                                const gdn_chunk* chunks, int nchunks, int nseq, int Hk, int Hv, float eps,
                                 int write_state, void* q, void* k, void* v, hipStream_t st) {
   const int C = (2 * Hk + Hv) * 128;
-  dim3 grid(nchunks, (C + 511) / 512);
+  dim3 grid(nchunks, (C + 511) / 512);   // nchunks: descriptors, or the derived slots
   if (act == GDN_F32) {
     hipLaunchKernelGGL(conv_post_kernel<float>, grid, dim3(64 * 64 / CPShape<float>::kTok), 0, st,
-                       static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks, C, Hk, Hv,
-                       eps, write_state, static_cast<float*>(q), static_cast<float*>(k), static_cast<float*>(v));
+                       static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks, nseq, C, Hk,
+                       Hv, eps, write_state, static_cast<float*>(q), static_cast<float*>(k), static_cast<float*>(v));
   } else {
     hipLaunchKernelGGL(conv_post_kernel<uint16_t>, grid, dim3(64 * 64 / CPShape<uint16_t>::kTok), 0, st,
-                       static_cast<const uint16_t*>(x), xs, w, bias, conv_state, has_init, cu, chunks, C, Hk,
-                       Hv, eps, write_state, static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
+                       static_cast<const uint16_t*>(x), xs, w, bias, conv_state, has_init, cu, chunks, nseq, C,
+                       Hk, Hv, eps, write_state, static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
                        static_cast<uint16_t*>(v));
   }
   return hipGetLastError();

@@ -21,7 +21,7 @@ hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const
 // bitwise equal to launch_conv followed by the post-conv with out = act).
 hipError_t launch_conv_postconv(const void* x, int64_t xs, int act, const float* w, const float* bias,
                                 float* conv_state, const uint8_t* has_init, const int32_t* cu,
-                                const gdn_chunk* chunks, int nchunks, int Hk, int Hv, float eps,
+                                const gdn_chunk* chunks, int nchunks, int nseq, int Hk, int Hv, float eps,
                                 int write_state, void* q, void* k, void* v, hipStream_t st);
 
 hipError_t launch_gates(const void* ba, int gate_act, const float* A_log, const float* dt_bias, int rows,

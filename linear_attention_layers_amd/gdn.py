@@ -216,13 +216,14 @@ def gdn_causal_conv_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.T
 
 def gdn_conv_postconv_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor],
                           conv_state: torch.Tensor, has_initial_state: Optional[torch.Tensor],
-                          cu_seqlens: torch.Tensor, chunks: torch.Tensor, write_state: bool,
+                          cu_seqlens: torch.Tensor, chunks: Optional[torch.Tensor], write_state: bool,
                           Hk: int, Hv: int, eps: float = 1e-6, q: Optional[torch.Tensor] = None,
                           k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
                           stream=None):
     """Conv and post-conv in one launch (C ABI gdn_conv_postconv_fwd);
     returns (q, k, v) in x's dtype, bitwise equal to gdn_causal_conv_fwd
-    followed by gdn_postconv_l2."""
+    followed by gdn_postconv_l2.  chunks=None (up to 64 sequences): the
+    launch derives the 64-token chunks from cu_seqlens itself."""
     N, C = x.shape
     _require(x.stride(1) == 1, "x rows must be contiguous")
     _require(C == (2 * Hk + Hv) * 128, "C must be (2 Hk + Hv) * 128")
@@ -239,7 +240,7 @@ def gdn_conv_postconv_fwd(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch
     _require(bias is None or bias.dtype == torch.float32, "bias: float32")
     _require(q.dtype == k.dtype == v.dtype == x.dtype, "q, k, v dtype must match x")
     _check(_conv_post(_ptr(x), x.stride(0), _code(x.dtype), _ptr(w), _ptr(bias), _ptr(conv_state),
-                      _ptr(has_initial_state), _ptr(cu_seqlens), _ptr(chunks), chunks.shape[0], nseq, N,
+                      _ptr(has_initial_state), _ptr(cu_seqlens), _ptr(chunks), 0 if chunks is None else chunks.shape[0], nseq, N,
                       Hk, Hv, 128, 128, float(eps), int(bool(write_state)), _ptr(q), _ptr(k), _ptr(v),
                       _stream(stream)), "gdn_conv_postconv_fwd")
     return q, k, v

@@ -217,7 +217,7 @@ def test_conv_postconv_validation():
 
     def call(**kw):
         a = list(base)
-        idx = {"xs": 1, "act": 2, "Hv": 13, "dk": 14, "eps": 16, "q": 18, "v": 20, "chunks": 8}
+        idx = {"xs": 1, "act": 2, "nseq": 10, "Hv": 13, "dk": 14, "eps": 16, "q": 18, "v": 20, "chunks": 8}
         for k_, v_ in kw.items():
             a[idx[k_]] = v_
         return fn(*a)
@@ -227,7 +227,8 @@ def test_conv_postconv_validation():
     assert call(xs=C - 8) == SHAPE
     assert call(eps=0.0) == SHAPE
     assert call(act=5) == DTYPE
-    assert call(chunks=None) == NULL
+    assert call(chunks=None, nseq=65) == SHAPE        # chunks derived in-kernel only up to 64 sequences
+    assert call(q=None) == NULL
     assert call(q=FAKE + (5 << 24) + 8) == ALIGN
     assert call(q=FAKE + 1024) == ALIAS                # q inside x
     assert call(v=FAKE + (6 << 24) + 4096) == ALIAS    # v inside k

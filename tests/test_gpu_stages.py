@@ -632,6 +632,34 @@ def test_conv_postconv_bitwise_equal_to_two_calls(case, write_state):
         assert torch.equal(ai, bi), f"{nm} differs in {(ai != bi).sum().item()} elements"
 
 
+DERIVE_CASES = [
+    ("bf16", I.GEO_TINY, [1, 2, 3, 63, 64, 65, 129, 200]),
+    ("bf16", I.GEO_TINY, [5, 0, 70, 0, 1, 0]),                      # empty sequences
+    ("f32", I.Geometry(Hk=2, Hv=2), [130, 7, 64, 128]),
+    ("bf16", I.GEO_TINY, [(7 * i) % 41 + 1 for i in range(64)]),    # 64 sequences
+    ("bf16", I.GEO_TINY, [64 * 3]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DERIVE_CASES)))
+def test_conv_postconv_derived_chunks_bitwise_equal_to_descriptors(case):
+    act, geo, lengths = DERIVE_CASES[case]
+    hinit = [i % 2 for i in range(len(lengths))]
+    lb = I.make_layer(geo, lengths, act, 860 + case, state_std=0.3, has_init=hinit)
+    print(f"derived chunks case {case}: {len(lengths)} sequences, N = {lb.N}", flush=True)
+    cu, hi, w, x = lb.cu_seqlens.to(DEV), lb.has_init.to(DEV), lb.conv_w.to(DEV), lb.x.to(DEV)
+    cs1 = lb.conv_state.to(DEV).contiguous()
+    cs2 = cs1.clone()
+    q1, k1, v1 = gdn.gdn_conv_postconv_fwd(x, w, None, cs1, hi, cu, gdn.gdn_make_chunks_device(cu, lb.N), True,
+                                           geo.Hk, geo.Hv, 1e-6)
+    q2, k2, v2 = gdn.gdn_conv_postconv_fwd(x, w, None, cs2, hi, cu, None, True, geo.Hk, geo.Hv, 1e-6)
+    torch.cuda.synchronize()
+    for a, b, nm in ((q1, q2, "q"), (k1, k2, "k"), (v1, v2, "v"), (cs1, cs2, "conv_state")):
+        ai = a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32)
+        bi = b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32)
+        assert torch.equal(ai, bi), f"{nm} differs in {(ai != bi).sum().item()} elements"
+
+
 def test_conv_postconv_f32_matches_oracle_chain():
     # the f32 arm against the oracle: conv in float64, rounded to float32,
     # then the post-conv in its documented order
