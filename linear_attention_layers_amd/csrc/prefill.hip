@@ -866,10 +866,14 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     __syncthreads();
     __syncthreads();
 
-    for (int c = 0; c < nc; ++c) {
+    // The loop runs two chunks per trip so that the factor buffer (ab =
+    // c & 1) and the V / o tile of each chunk are compile-time constants:
+    // their LDS offsets fold into the read instructions (32k prefill -2%).
+    auto iteration = [&](int c, auto ab_c) __attribute__((always_inline)) {
+      constexpr int ab = decltype(ab_c)::value;   // c & 1
       const int n = chunk_len(c);
       const int64_t c0 = bos + BT * c;
-      const int kb = c % 3, ab = c & 1;
+      const int kb = c % 3;
       const uint16_t* Kc = sm.K[kb];
       const uint16_t* Qc = sm.Q[kb];
       const uint16_t* ATc = sm.AT[ab];
@@ -878,9 +882,9 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       const float gamma_last = __builtin_amdgcn_exp2f(Wc[n - 1]);
 
       float vv[VB][4][4];
-      get_v(c & 1, vv[0]);
-      if (WO && c > 0) read_o((c + 1) & 1);
-      put_v((c + 1) & 1);
+      get_v(ab, vv[0]);
+      if (WO && c > 0) read_o(ab ^ 1);
+      put_v(ab ^ 1);
       load_v(c + 2);
       if (WO && c > 0) store_o();
 
@@ -1097,9 +1101,13 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
             opk[b][ib] = u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
           }
         }
-        stage_o(c & 1);
+        stage_o(ab);
       }
       __syncthreads();
+    };
+    for (int c = 0; c < nc; c += 2) {
+      iteration(c, std::integral_constant<int, 0>{});
+      if (c + 1 < nc) iteration(c + 1, std::integral_constant<int, 1>{});
     }
     if (WO) {
       read_o((nc - 1) & 1);
