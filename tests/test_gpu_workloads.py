@@ -132,6 +132,37 @@ def test_varlen_prefill_bf16_full_size():
         _check_recurrence(lb, out, heads, TL.REC_BF16)
 
 
+def _bench_path_equals_separate_calls(lb, out):
+    """The benchmark's launch configuration (conv and post-conv in one launch
+    with the chunks derived from cu_seqlens, then the prefill) gives bitwise
+    the outputs of the separate calls that the other tests check against
+    the oracle."""
+    x, w = lb.x.to(DEV), lb.conv_w.to(DEV)
+    cs = lb.conv_state.to(DEV).contiguous()
+    st = lb.state.to(DEV).contiguous()
+    q, k, v = gdn.gdn_conv_postconv_fwd(x, w, TL.dev(lb.conv_b), cs, out["hi"], out["cu"], None, True,
+                                        lb.geo.Hk, lb.geo.Hv, 1e-6)
+    o = gdn.gdn_delta_rule_prefill(q, k, v, out["g"], out["beta"], out["cu"], st, out["hi"])
+    torch.cuda.synchronize()
+    for a, b, nm in ((q, out["q"], "q"), (k, out["k"], "k"), (v, out["v"], "v"), (o, out["o"], "o"),
+                     (cs, out["conv_state"], "conv_state"), (st, out["state"], "state")):
+        ai = a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32)
+        bi = b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32)
+        assert torch.equal(ai, bi), f"{nm} differs in {(ai != bi).sum().item()} elements"
+
+
+def test_varlen_prefill_bf16_full_size_bench_path():
+    lb = I.varlen_prefill()
+    out = TL.gpu_layer(lb)
+    _bench_path_equals_separate_calls(lb, out)
+
+
+def test_long_prefill_32k_bench_path():
+    lb = I.long_prefill()
+    out = TL.gpu_layer(lb)
+    _bench_path_equals_separate_calls(lb, out)
+
+
 def test_long_prefill_32k_sampled():
     lb = I.long_prefill()
     out = TL.gpu_layer(lb)
