@@ -328,3 +328,44 @@ def test_gates_validation():
     assert call(beta=FAKE + (3 << 24) + 16) == ALIAS     # overlaps g
     assert call(g=FAKE + 40) == ALIAS                    # inside ba
     assert call(N=0) == OK
+
+
+def _derived_chunks(cu, nslots):
+    """Host restatement of the fused conv launch's slot map: slot j belongs
+    to the last sequence s with floor(cu[s] / 64) + s <= j, as its chunk
+    j - f(s) when that chunk exists."""
+    nseq = len(cu) - 1
+    f = [cu[s] // 64 + s for s in range(nseq)]
+    out = []
+    for j in range(nslots):
+        s = max(t for t in range(nseq) if f[t] <= j)
+        c = j - f[s]
+        nc = -(-(cu[s + 1] - cu[s]) // 64)
+        if c < nc:
+            b = cu[s] + 64 * c
+            out.append((s, b, min(b + 64, cu[s + 1]), (1 if c == 0 else 0) | (2 if c == nc - 1 else 0)))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_derived_chunk_slots_give_the_descriptor_list(seed):
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.integers(1, 65))
+    lengths = [int(v) for v in rng.integers(0, 300, nseq)]
+    lengths[int(rng.integers(0, nseq))] = int(rng.integers(1, 1000))   # at least one token
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    got = _derived_chunks(cu, cu[-1] // 64 + nseq)
+    ref = [tuple(int(v) for v in row) for row in O.make_chunks(cu, 64)]
+    assert got == ref
+
+
+@pytest.mark.parametrize("lengths", [[1] * 64, [64] * 64, [63] * 64, [65, 63, 1, 127, 0, 129], [0, 0, 5], [4096]])
+def test_derived_chunk_slots_edge_batches(lengths):
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    got = _derived_chunks(cu, cu[-1] // 64 + len(lengths))
+    ref = [tuple(int(v) for v in row) for row in O.make_chunks(cu, 64)]
+    assert got == ref
