@@ -292,6 +292,138 @@ def test_f32_arm_is_close_to_the_float64_definition():
         np.testing.assert_allclose(a, b, rtol=6e-7, atol=1e-30)
 
 
+def _l2_scale_cases():
+    """Hand-derived float32 cases of tests/golden/l2_scale_cases.txt as
+    (name, eps, y head [128] float64, expected q_hat [128] float32)."""
+    def parse(spec, conv):
+        vals, fill = {}, None
+        for part in spec.split(";"):
+            key, val = [p.strip() for p in part.split(":")]
+            if key == "rest":
+                fill = conv(val)
+            else:
+                vals[int(key)] = conv(val)
+        return [vals.get(i, fill) for i in range(128)]
+
+    hexf = lambda h: np.frombuffer(bytes.fromhex(h)[::-1], dtype=np.float32)[0]  # noqa: E731
+    cases = []
+    with open(os.path.join(GOLDEN, "l2_scale_cases.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, eps, yspec, qspec = [p.strip() for p in line.split("|")]
+            cases.append((name, float(eps), np.array(parse(yspec, float), dtype=np.float64),
+                          np.array(parse(qspec, hexf), dtype=np.float32)))
+    return cases
+
+
+def _l2_f32_pins_pass(fn):
+    """True when fn(y, Hk, Hv, dk, dv, eps) -> (q, k, v) float32 passes every
+    pin of the float32 post-conv arm below."""
+    d = 128
+    # 1. hand-derived values: the head pattern in q, k and v of one token
+    for name, eps, yh, want in _l2_scale_cases():
+        y = np.concatenate([yh, yh, yh])[None]
+        q, k, v = fn(y, 1, 1, d, d, eps)
+        for got in (q[0, 0], k[0, 0]):
+            if got.view(np.uint32).tolist() != want.view(np.uint32).tolist():
+                return False
+        if not np.array_equal(v[0, 0], yh.astype(np.float32)):
+            return False
+    # 2. closed form with an eps comparable to the sum of squares:
+    #    |q_hat|^2 = sigma / (sigma + eps), sigma the float64 sum of the
+    #    float32 SiLU values (the arm's own rounding of s)
+    r = np.random.default_rng(55)
+    Hk, Hv = 3, 2
+    y = r.standard_normal((40, 2 * Hk * d + Hv * d)) * 0.12
+    eps = 0.25
+    q, k, _ = fn(y, Hk, Hv, d, d, eps)
+    s = O.silu(y).astype(np.float32).astype(np.float64)
+    for got, lo in ((q, 0), (k, Hk * d)):
+        raw = s[:, lo:lo + Hk * d].reshape(-1, Hk, d)
+        sig = np.sum(raw * raw, axis=-1)
+        if not (0.3 < sig.min() and sig.max() < 3.0):
+            return False        # the case is meant to have sigma near eps
+        nrm2 = np.sum(got.astype(np.float64) ** 2, axis=-1)
+        if not np.allclose(nrm2, sig / (sig + eps), rtol=2e-6, atol=0):
+            return False
+    return True
+
+
+def test_l2_f32_pins_accept_the_oracle():
+    assert _l2_f32_pins_pass(O.postconv_l2_f32_tree)
+
+
+def _mutant_l2_f32(kind):
+    def fn(y, Hk, Hv, dk, dv, eps):
+        s = O.silu(y).astype(np.float32)
+        q, k, v = O.split_heads(s, Hk, Hv, dk, dv)
+        e = np.float32(eps)
+
+        def norm(a):
+            sig = O.tree_sum_f32((a * a).astype(np.float32))
+            if kind == "eps_outside":
+                den = (np.sqrt(sig).astype(np.float32) + e).astype(np.float32)
+                return (a * (np.float32(1) / den).astype(np.float32)[..., None]).astype(np.float32)
+            root = np.sqrt((sig + e).astype(np.float32)).astype(np.float32)
+            if kind == "divide":
+                return (a / root[..., None]).astype(np.float32)
+            if kind == "no_eps":
+                root = np.sqrt(sig).astype(np.float32)
+            inv = (np.float32(1) / root).astype(np.float32)
+            return (a * inv[..., None]).astype(np.float32)
+        return norm(q), norm(k), v.astype(np.float32)
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["eps_outside", "divide", "no_eps"])
+def test_l2_f32_pins_catch_planted_mutation(kind):
+    assert not _l2_f32_pins_pass(_mutant_l2_f32(kind))
+
+
+def test_split_heads_region_offsets():
+    # One token, Hk = 2, Hv = 3, dk = dv = 8: every channel carries its own
+    # code region*100 + head*10 + index, so each output element names where
+    # it was taken from: q from channels [0, 16), k from [16, 32), v from
+    # [32, 56), head h of each region at offset h * 8 within it.
+    Hk, Hv, d = 2, 3, 8
+    y = np.concatenate([[100 * 1 + 10 * h + i for h in range(Hk) for i in range(d)],
+                        [100 * 2 + 10 * h + i for h in range(Hk) for i in range(d)],
+                        [100 * 3 + 10 * h + i for h in range(Hv) for i in range(d)]]).astype(np.float64)
+    assert y.shape == (2 * Hk * d + Hv * d,)
+    q, k, v = O.split_heads(y[None], Hk, Hv, d, d)
+    assert q.shape == (1, Hk, d) and k.shape == (1, Hk, d) and v.shape == (1, Hv, d)
+    for h in range(Hk):
+        assert q[0, h].tolist() == [100 + 10 * h + i for i in range(d)]
+        assert k[0, h].tolist() == [200 + 10 * h + i for i in range(d)]
+    for h in range(Hv):
+        assert v[0, h].tolist() == [300 + 10 * h + i for i in range(d)]
+
+
+def test_postconv_takes_each_region_from_its_offset():
+    # Distinct constants per region in the SiLU identity region (y >= 17):
+    # v passes them through unchanged, and a q or k head holding a single
+    # spike normalises to that spike's unit vector.  Reading k or v from a
+    # wrong offset moves a spike or changes a constant.
+    Hk, Hv, d = 2, 3, 16
+    y = np.zeros((1, 2 * Hk * d + Hv * d))
+    for h in range(Hk):
+        y[0, h * d + h] = 20.0 + h                       # q head h: spike at h
+        y[0, Hk * d + h * d + (h + 5)] = 30.0 + h        # k head h: spike at h + 5
+    for h in range(Hv):
+        y[0, 2 * Hk * d + h * d: 2 * Hk * d + (h + 1) * d] = 40.0 + h
+    for fn in (lambda a: O.postconv_l2(a, Hk, Hv, d, d, 1e-6),
+               lambda a: O.postconv_l2_f32_tree(a, Hk, Hv, d, d, 1e-6)):
+        q, k, v = fn(y)
+        for h in range(Hk):
+            assert int(np.argmax(q[0, h])) == h and np.count_nonzero(q[0, h]) == 1
+            assert int(np.argmax(k[0, h])) == h + 5 and np.count_nonzero(k[0, h]) == 1
+            assert abs(float(q[0, h, h]) - 1.0) < 1e-6 and abs(float(k[0, h, h + 5]) - 1.0) < 1e-6
+        for h in range(Hv):
+            assert np.all(v[0, h] == 40.0 + h)
+
+
 # ---------------------------------------------------------------------------
 # a4/a5: the gated delta rule
 # ---------------------------------------------------------------------------
