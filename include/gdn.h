@@ -45,6 +45,13 @@
  *   - has_initial_state[nseq] (device, uint8; NULL = all set): when 0, the
  *     sequence starts from zero conv rows and a zero recurrent state, and
  *     the stored buffers are not read (they may hold anything, NaN included).
+ *   - Empty sequences (cu[s+1] == cu[s]): the final conv rows and recurrent
+ *     state are the initial ones.  With has_initial_state[s] = 1 they are left
+ *     bit-identical; with 0 every call that writes a final state (the conv
+ *     with write_state, the prefill, a committing step, the fused step) writes
+ *     zeros, as for a sequence whose tokens are all skipped.  N = 0 with
+ *     nseq > 0 is valid: only those zero writes happen (token buffers may be
+ *     NULL then).  gdn_commit with n_keep[s] = 0 writes nothing.
  *   - Errors: the host validates arguments before any launch and returns a
  *     gdn_status; gdn_last_error() gives a message (thread-local).  No
  *     exception crosses the ABI.
@@ -113,14 +120,19 @@ const char* gdn_last_error(void);
  * sequences emit nothing ("New issue #305": exact chunks, first-chunk /
  * last-chunk roles).  Integer work, bit-exact.
  *
+ * chunk_len must lie in 3 .. 64 (GDN_CHUNK_LEN): the conv kernels cover at
+ * most 64 tokens per descriptor, and a chunk that does not start its
+ * sequence reads the 3 rows before it from the same sequence.  Other
+ * values are GDN_ERR_SHAPE (and capacity 0).
+ *
  * gdn_chunk_capacity: an upper bound on the number of chunks of any batch
  * with N tokens in nseq sequences: floor((N + nseq*(chunk_len-1)) /
- * chunk_len).
+ * chunk_len); 0 for invalid arguments.
  *
  * gdn_make_chunks (host): reads cu_seqlens (host, nseq+1 entries), writes
  * at most `cap` descriptors to out (host).  Returns the count (>= 0), or
- * -GDN_ERR_* (NULL pointer, nseq < 0, chunk_len < 1, cu not nondecreasing
- * from 0, or more than cap chunks).
+ * -GDN_ERR_* (NULL pointer, nseq < 0, chunk_len outside 3..64, cu not
+ * nondecreasing from 0, or more than cap chunks).
  *
  * gdn_make_chunks_device: the same list built on the GPU from a device
  * cu_seqlens, written to out (device) with exactly `cap` slots; slots past
@@ -141,11 +153,15 @@ int gdn_make_chunks_device(const int32_t* cu_seqlens, int nseq, int chunk_len,
  * multiplies the current token.
  * When write_state != 0, conv_state[s] becomes the last 3 rows of
  * [stored rows ; x of sequence s]; otherwise conv_state is not written.
- * Exactly one wave per (sequence, 512-channel group) touches conv_state:
+ * Exactly one wave per (sequence, 256-channel group) touches conv_state:
  * wave 0 of the sequence's first chunk reads the stored rows and, later in
  * the same lanes' program order, writes the final rows, so the in-place
- * update has no cross-workgroup race.  Non-first chunks must start at least
- * 3 tokens into their sequence (true for any chunk_len >= 3).
+ * update has no cross-workgroup race.  Empty sequences have no chunk; one
+ * extra workgroup column writes their zero rows (see "Empty sequences").
+ * Descriptor preconditions (device data, not checked): each covers at most
+ * 64 tokens of one sequence, and one that is not its sequence's first
+ * starts at least 3 tokens into it; gdn_make_chunks* with chunk_len in
+ * 3..64 produce such lists.
  *   x           (device) [N][x_row_stride] act, x_row_stride >= C, rows
  *               16-byte aligned
  *   w           (device) float [C][4];  bias (device) float [C] or NULL (0)
@@ -181,10 +197,10 @@ int gdn_postconv_l2(const void* y, int64_t y_row_stride, int in, int N,
 
 /* ---- 3b. conv and post-conv in one launch ---------------------------------
  * gdn_causal_conv_fwd followed by gdn_postconv_l2 (out = act), with y kept
- * on chip: each lane forms y for its 4 channels, rounds it to the
+ * on chip: each lane forms y for 8 adjacent channels, rounds it to the
  * activation dtype as the stored y would be, and applies SiLU, the head's
- * sum of squares in the documented order (the post-conv's 16-lane tree,
- * taken over the conv's 32 lanes per head) and the L2 scale on q and k.
+ * sum of squares in the documented order (one 128-channel head per 16-lane
+ * row, the post-conv kernel's tree) and the L2 scale on q and k.
  * Results are bitwise equal to the two calls ("perf(gdn): optimize
  * post-conv and causal-conv kernels", "What I verified": the fixed order is
  * what makes that checkable).  conv_state is updated as by the conv.

@@ -47,6 +47,11 @@ int check_heads(int Hk, int Hv, int dk, int dv) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// The conv kernels cover at most 64 tokens per descriptor, and a non-first
+// chunk reads the 3 rows before it from its own sequence, so chunks are
+// 3 .. 64 tokens long.
+bool valid_chunk_len(int chunk_len) { return chunk_len >= 3 && chunk_len <= GDN_CHUNK_LEN; }
+
 int check_recurrence(const void* q, const void* k, const void* v, int act, const float* g,
                      const float* beta, const int32_t* cu, int nseq, int N, int Hk, int Hv,
                      int dk, int dv, const float* state, const void* o) {
@@ -93,14 +98,14 @@ const char* gdn_status_string(int status) {
 const char* gdn_last_error(void) { return g_last_error; }
 
 int gdn_chunk_capacity(int N, int nseq, int chunk_len) {
-  if (N < 0 || nseq < 0 || chunk_len < 1) return 0;
+  if (N < 0 || nseq < 0 || !valid_chunk_len(chunk_len)) return 0;
   const long long cap = ((long long)N + (long long)nseq * (chunk_len - 1)) / chunk_len;
   return cap > 0x7fffffff ? 0x7fffffff : (int)cap;
 }
 
 int gdn_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out, int cap) {
   if (nseq < 0) return -fail(GDN_ERR_SHAPE, "nseq < 0");
-  if (chunk_len < 1) return -fail(GDN_ERR_SHAPE, "chunk_len < 1");
+  if (!valid_chunk_len(chunk_len)) return -fail(GDN_ERR_SHAPE, "chunk_len must be in 3..64 (got %d)", chunk_len);
   if (cu == nullptr) return -fail(GDN_ERR_NULL, "cu_seqlens is NULL");
   if (cu[0] != 0) return -fail(GDN_ERR_SHAPE, "cu_seqlens[0] must be 0");
   int count = 0;
@@ -123,7 +128,7 @@ int gdn_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out, 
 int gdn_make_chunks_device(const int32_t* cu, int nseq, int chunk_len, gdn_chunk* out, int cap,
                            void* stream) {
   if (nseq < 0 || cap < 0) return -fail(GDN_ERR_SHAPE, "nseq or cap < 0");
-  if (chunk_len < 1) return -fail(GDN_ERR_SHAPE, "chunk_len < 1");
+  if (!valid_chunk_len(chunk_len)) return -fail(GDN_ERR_SHAPE, "chunk_len must be in 3..64 (got %d)", chunk_len);
   if (cap == 0) return GDN_OK;
   if (cu == nullptr || out == nullptr) return -fail(GDN_ERR_NULL, "cu_seqlens and out are required");
   const int st = launched(gdn::launch_make_chunks(cu, nseq, chunk_len, out, cap, as_stream(stream)),
@@ -138,19 +143,22 @@ int gdn_causal_conv_fwd(const void* x, int64_t xs, int act, const float* w, cons
   if (!valid_dtype(act)) return fail(GDN_ERR_DTYPE, "unsupported activation dtype %d", act);
   if (N < 0 || nseq < 0 || nchunks < 0 || C < 8 || C % 8 != 0 || xs < C)
     return fail(GDN_ERR_SHAPE, "need N, nseq, nchunks >= 0, C a positive multiple of 8, x_row_stride >= C");
-  if (N == 0 || nseq == 0 || nchunks == 0) return GDN_OK;
-  if (!x || !w || !conv_state || !cu || !chunks || !y) return fail(GDN_ERR_NULL, "missing required pointer");
+  // with no tokens only the final rows of empty sequences are written
+  if (N == 0) nchunks = 0;
+  if (nseq == 0 || (nchunks == 0 && !write_state)) return GDN_OK;
+  if (!conv_state || !cu) return fail(GDN_ERR_NULL, "conv_state and cu_seqlens are required");
+  if (N > 0 && (!x || !w || !chunks || !y)) return fail(GDN_ERR_NULL, "x, w, chunks and y are required");
   const int e = elem_bytes(act);
   if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || !aligned16(conv_state) ||
       !aligned16(y) || (bias && !aligned16(bias)))
     return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state and y must be 16-byte aligned");
   const size_t ny = (size_t)N * C * e;
-  const size_t nx = ((size_t)(N - 1) * xs + C) * e;
+  const size_t nx = N > 0 ? ((size_t)(N - 1) * xs + C) * e : 0;
   const size_t ns = (size_t)nseq * 3 * C * 4;
   if (overlaps(y, ny, x, nx) || overlaps(y, ny, conv_state, ns) || overlaps(y, ny, w, (size_t)C * 16))
     return fail(GDN_ERR_ALIAS, "y must not overlap x, w or conv_state");
   if (overlaps(conv_state, ns, x, nx)) return fail(GDN_ERR_ALIAS, "conv_state must not overlap x");
-  return launched(gdn::launch_conv(x, xs, act, w, bias, conv_state, has_init, cu, chunks, nchunks, C,
+  return launched(gdn::launch_conv(x, xs, act, w, bias, conv_state, has_init, cu, chunks, nchunks, nseq, C,
                                    write_state, y, as_stream(stream)),
                   "causal_conv");
 }
@@ -172,14 +180,16 @@ int gdn_conv_postconv_fwd(const void* x, int64_t xs, int act, const float* w, co
     if (nseq > 64) return fail(GDN_ERR_SHAPE, "chunks may be NULL only for nseq <= 64 (got %d)", nseq);
     nchunks = N / 64 + nseq;
   }
-  if (N == 0 || nseq == 0 || nchunks == 0) return GDN_OK;
-  if (!x || !w || !conv_state || !cu || !q || !k || !v)
-    return fail(GDN_ERR_NULL, "missing required pointer");
+  // with no tokens only the final rows of empty sequences are written
+  if (N == 0) nchunks = 0;
+  if (nseq == 0 || (nchunks == 0 && !write_state)) return GDN_OK;
+  if (!conv_state || !cu) return fail(GDN_ERR_NULL, "conv_state and cu_seqlens are required");
+  if (N > 0 && (!x || !w || !q || !k || !v)) return fail(GDN_ERR_NULL, "x, w, q, k and v are required");
   const int e = elem_bytes(act);
   if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || !aligned16(conv_state) ||
       (bias && !aligned16(bias)) || !aligned16(q) || !aligned16(k) || !aligned16(v))
     return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state, q, k and v must be 16-byte aligned");
-  const size_t nx = ((size_t)(N - 1) * xs + C) * e, ns = (size_t)nseq * 3 * C * 4;
+  const size_t nx = N > 0 ? ((size_t)(N - 1) * xs + C) * e : 0, ns = (size_t)nseq * 3 * C * 4;
   const size_t nq = (size_t)N * Hk * dk * e, nv = (size_t)N * Hv * dv * e;
   struct Buf { const void* p; size_t n; } out[4] = {{q, nq}, {k, nq}, {v, nv}, {conv_state, ns}};
   for (int i = 0; i < 4; ++i) {
@@ -267,7 +277,9 @@ int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act, co
                         int dk, int dv, float* state, const uint8_t* has_init, void* o,
                         int commit_state, void* stream) {
   int st = check_recurrence(q, k, v, act, g, beta, cu, nseq, N, Hk, Hv, dk, dv, state, o);
-  if (st != GDN_OK || nseq == 0 || N == 0) return st;
+  // with no tokens a committing step still writes the (zero) states of
+  // sequences without an initial state
+  if (st != GDN_OK || nseq == 0 || (N == 0 && !commit_state)) return st;
   return launched(gdn::launch_step(q, k, v, act, g, beta, cu, nseq, Hk, Hv, state, has_init, o,
                                    commit_state, as_stream(stream)),
                   "delta_rule_step");
@@ -287,15 +299,16 @@ int gdn_decode_fused(const void* x, int64_t xs, int act, const float* w, const f
   const int C = 2 * Hk * dk + Hv * dv;
   if (xs < C) return fail(GDN_ERR_SHAPE, "x_row_stride must be >= C");
   if (xs > (int64_t)(1 << 24)) return fail(GDN_ERR_SHAPE, "x_row_stride above 2^24 elements");
-  if (nseq == 0 || N == 0) return GDN_OK;
-  if (!x || !w || !conv_state || !cu || !g || !beta || !state || !o)
-    return fail(GDN_ERR_NULL, "x, w, conv_state, cu_seqlens, g, beta, state and o are required");
+  if (nseq == 0 || (N == 0 && !write_conv_state && !commit_state)) return GDN_OK;
+  if (!conv_state || !cu || !state) return fail(GDN_ERR_NULL, "conv_state, cu_seqlens and state are required");
+  if (N > 0 && (!x || !w || !g || !beta || !o))
+    return fail(GDN_ERR_NULL, "x, w, g, beta and o are required");
   const size_t e = elem_bytes(act);
   if (!aligned16(x) || ((size_t)xs * e) % 16 != 0 || !aligned16(w) || (bias && !aligned16(bias)) ||
       !aligned16(conv_state) || !aligned16(state) || !aligned16(o) || (k_out && !aligned16(k_out)) ||
       (v_out && !aligned16(v_out)))
     return fail(GDN_ERR_ALIGN, "x rows, w, bias, conv_state, state, o, k_out and v_out must be 16-byte aligned");
-  const size_t nx = ((size_t)(N - 1) * xs + C) * e, ncs = (size_t)nseq * 3 * C * 4;
+  const size_t nx = N > 0 ? ((size_t)(N - 1) * xs + C) * e : 0, ncs = (size_t)nseq * 3 * C * 4;
   const size_t no = (size_t)N * Hv * dv * e, ns = (size_t)nseq * Hv * dv * dk * 4;
   const size_t nk = k_out ? (size_t)N * Hk * dk * e : 0, nv = v_out ? (size_t)N * Hv * dv * e : 0;
   struct Buf { const void* p; size_t n; } out[5] = {{o, no}, {state, ns}, {conv_state, ncs}, {k_out, nk}, {v_out, nv}};

@@ -142,13 +142,44 @@ __global__ __launch_bounds__(256) void make_chunks_kernel(const int32_t* __restr
   }
 }
 
+// ------------------------------------------------- empty sequences
+// A sequence with no tokens has no chunk, so no chunk workgroup owns its
+// conv_state.  Its final rows are its initial rows: unchanged with an
+// initial state, zeros without one.  One extra workgroup column (launched
+// only when the final rows are written) takes the second case: wave 0
+// finds the empty sequences without an initial state 64 at a time (lane =
+// sequence, one ballot) and its lanes store zeros into the three rows of
+// their CPL channels of the column's channel group.
+template <int CPL>
+__device__ __forceinline__ void zero_empty_conv_rows(float* conv_state, const uint8_t* __restrict__ has_init,
+                                                     const int32_t* __restrict__ cu, int nseq, int C, int c0,
+                                                     int lane) {
+  for (int s0 = 0; s0 < nseq; s0 += 64) {
+    const int s = s0 + lane;
+    const bool empty = s < nseq && cu[s + 1] == cu[s] && !seq_flag(has_init, s);
+    uint64_t m = __builtin_amdgcn_ballot_w64(empty);
+    while (m != 0) {
+      const int se = s0 + __builtin_ctzll(m);
+      m &= m - 1;
+      if (c0 < C) {
+        float* st = conv_state + (int64_t)se * 3 * C + c0;
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+          for (int i = 0; i < CPL; i += 4)
+            *reinterpret_cast<float4*>(st + (int64_t)r * C + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- the conv
-// Workgroup = (chunk slot, group of 512 channels); wave w handles tokens
-// [16 w, 16 w + 16) of the chunk and lane l channels 8 l .. 8 l + 7 of the
+// Workgroup = (chunk slot, group of 256 channels); wave w handles tokens
+// [16 w, 16 w + 16) of the chunk and lane l channels 4 l .. 4 l + 3 of the
 // group.  A lane issues its 3 halo rows and its 16 token rows up front (19
-// independent 16-byte loads), then computes and stores 16 outputs.  Only
-// wave 0 of a sequence's first chunk touches conv_state (see the file
-// comment).
+// independent loads), then computes and stores 16 outputs.  Only wave 0 of
+// a sequence's first chunk touches conv_state (see the file comment); the
+// column past the last slot clears the rows of empty sequences.
 // Four adjacent activations in storage form.
 template <class T> struct Act4;
 template <> struct Act4<float> {
@@ -176,11 +207,15 @@ template <class T>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
     float* conv_state, const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu,
-    const gdn_chunk* __restrict__ chunks, int C, int write_state, T* __restrict__ y) {
+    const gdn_chunk* __restrict__ chunks, int nslots, int nseq, int C, int write_state, T* __restrict__ y) {
   using A = Act4<T>;
-  const gdn_chunk ch = chunks[blockIdx.x];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int c0 = (blockIdx.y * 64 + lane) * kConvChannelsPerLane;
+  if ((int)blockIdx.x == nslots) {   // launched only when write_state
+    if (wave == 0) zero_empty_conv_rows<kConvChannelsPerLane>(conv_state, has_init, cu, nseq, C, c0, lane);
+    return;
+  }
+  const gdn_chunk ch = chunks[blockIdx.x];
   if (ch.seq < 0 || c0 >= C) return;
   const int s = ch.seq;
   const int t_begin = ch.begin + kConvTokensPerWave * wave;
@@ -320,13 +355,17 @@ template <class T>
 __global__ __launch_bounds__(64 * 64 / CPShape<T>::kTok) void conv_post_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
     float* conv_state, const uint8_t* __restrict__ has_init, const int32_t* __restrict__ cu,
-    const gdn_chunk* __restrict__ chunks, int nseq, int C, int Hk, int Hv, float eps, int write_state,
-    T* __restrict__ q, T* __restrict__ k, T* __restrict__ v) {
+    const gdn_chunk* __restrict__ chunks, int nslots, int nseq, int C, int Hk, int Hv, float eps,
+    int write_state, T* __restrict__ q, T* __restrict__ k, T* __restrict__ v) {
   constexpr int TPW = CPShape<T>::kTok;
   using AT = Act<T>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const gdn_chunk ch = chunks != nullptr ? chunks[blockIdx.x] : derive_chunk(cu, nseq, blockIdx.x, lane);
   const int c0 = (blockIdx.y * 64 + lane) * 8;
+  if ((int)blockIdx.x == nslots) {   // launched only when write_state
+    if (wave == 0) zero_empty_conv_rows<8>(conv_state, has_init, cu, nseq, C, c0, lane);
+    return;
+  }
+  const gdn_chunk ch = chunks != nullptr ? chunks[blockIdx.x] : derive_chunk(cu, nseq, blockIdx.x, lane);
   if (ch.seq < 0 || c0 >= C) return;   // whole 16-lane rows: C is a multiple of 128
   const int s = ch.seq;
   const int t_begin = ch.begin + TPW * wave;
@@ -461,15 +500,19 @@ hipError_t launch_conv_postconv(const void* x, int64_t xs, int act, const float*
                                 const gdn_chunk* chunks, int nchunks, int nseq, int Hk, int Hv, float eps,
                                 int write_state, void* q, void* k, void* v, hipStream_t st) {
   const int C = (2 * Hk + Hv) * 128;
-  dim3 grid(nchunks, (C + 511) / 512);   // nchunks: descriptors, or the derived slots
+  // nchunks slots (descriptors, or the derived slots), and when the final
+  // rows are written one more column for the empty sequences
+  dim3 grid(nchunks + (write_state ? 1 : 0), (C + 511) / 512);
+  if (grid.x == 0) return hipSuccess;
   if (act == GDN_F32) {
     hipLaunchKernelGGL(conv_post_kernel<float>, grid, dim3(64 * 64 / CPShape<float>::kTok), 0, st,
-                       static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks, nseq, C, Hk,
-                       Hv, eps, write_state, static_cast<float*>(q), static_cast<float*>(k), static_cast<float*>(v));
+                       static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks, nchunks, nseq,
+                       C, Hk, Hv, eps, write_state, static_cast<float*>(q), static_cast<float*>(k),
+                       static_cast<float*>(v));
   } else {
     hipLaunchKernelGGL(conv_post_kernel<uint16_t>, grid, dim3(64 * 64 / CPShape<uint16_t>::kTok), 0, st,
-                       static_cast<const uint16_t*>(x), xs, w, bias, conv_state, has_init, cu, chunks, nseq, C,
-                       Hk, Hv, eps, write_state, static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
+                       static_cast<const uint16_t*>(x), xs, w, bias, conv_state, has_init, cu, chunks, nchunks,
+                       nseq, C, Hk, Hv, eps, write_state, static_cast<uint16_t*>(q), static_cast<uint16_t*>(k),
                        static_cast<uint16_t*>(v));
   }
   return hipGetLastError();
@@ -477,17 +520,20 @@ hipError_t launch_conv_postconv(const void* x, int64_t xs, int act, const float*
 
 hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const float* bias,
                        float* conv_state, const uint8_t* has_init, const int32_t* cu,
-                       const gdn_chunk* chunks, int nchunks, int C, int write_state, void* y,
+                       const gdn_chunk* chunks, int nchunks, int nseq, int C, int write_state, void* y,
                        hipStream_t st) {
-  dim3 grid(nchunks, (C + kConvChannelsPerBlock - 1) / kConvChannelsPerBlock);
+  // one column per chunk slot, and one for the empty sequences when the
+  // final rows are written
+  dim3 grid(nchunks + (write_state ? 1 : 0), (C + kConvChannelsPerBlock - 1) / kConvChannelsPerBlock);
+  if (grid.x == 0) return hipSuccess;
   if (act == GDN_F32) {
     hipLaunchKernelGGL(conv_kernel<float>, grid, dim3(kConvThreads), 0, st,
                        static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks,
-                       C, write_state, static_cast<float*>(y));
+                       nchunks, nseq, C, write_state, static_cast<float*>(y));
   } else {
     hipLaunchKernelGGL(conv_kernel<uint16_t>, grid, dim3(kConvThreads), 0, st,
                        static_cast<const uint16_t*>(x), xs, w, bias, conv_state, has_init, cu,
-                       chunks, C, write_state, static_cast<uint16_t*>(y));
+                       chunks, nchunks, nseq, C, write_state, static_cast<uint16_t*>(y));
   }
   return hipGetLastError();
 }

@@ -15,7 +15,7 @@ hipError_t launch_make_chunks(const int32_t* cu, int nseq, int chunk_len, gdn_ch
 
 hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const float* bias,
                        float* conv_state, const uint8_t* has_init, const int32_t* cu,
-                       const gdn_chunk* chunks, int nchunks, int C, int write_state, void* y,
+                       const gdn_chunk* chunks, int nchunks, int nseq, int C, int write_state, void* y,
                        hipStream_t st);
 // The conv with the post-conv step fused (q, k, v written instead of y;
 // bitwise equal to launch_conv followed by the post-conv with out = act).

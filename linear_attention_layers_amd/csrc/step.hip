@@ -96,6 +96,16 @@ __device__ __forceinline__ void store_state(float* base, int v0, int r16, int kg
           make_float4(st[b][cb][0], st[b][cb][1], st[b][cb][2], st[b][cb][3]);
 }
 
+// This wave's state rows set to zero (an empty sequence without an initial
+// state, when the final state is written).
+__device__ __forceinline__ void store_zero_state(float* base, int v0, int r16, int kg) {
+#pragma unroll
+  for (int b = 0; b < kRB; ++b)
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      *reinterpret_cast<float4*>(base + (v0 + 16 * b + r16) * 128 + 16 * cb + 4 * kg) = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 // Token inputs of one block of a window, in registers: this wave's
 // 32-column slice of the K and Q rows (staged to LDS for every wave), and
 // what the wave alone reads.
@@ -363,8 +373,12 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_ker
   const int v0 = kRows * wave;
   const int bos = cu[s], len = cu[s + 1] - bos;
   const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
-  if (len <= 0) return;
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
+  if (len <= 0) {
+    // no tokens: the final state is the initial one, zero without a flag
+    if (commit_state && !init) store_zero_state(base, v0, r16, kg);
+    return;
+  }
   BlockIn<T, true> in;
   load_block<T, true>(in, lane, wave, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
   f32x4 st[kRB][8];
@@ -447,7 +461,6 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
   const int C = (2 * Hk + Hv) * 128;
   const int bos = cu[s], len = cu[s + 1] - bos;
   const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
-  if (len <= 0) return;
   float* cs = conv_state + (int64_t)s * 3 * C;
   // global channel of channel c (0 .. CH-1) of this workgroup: slots 0, 1
   // are the q and k heads of k-head kh, slots 2.. its v heads
@@ -456,6 +469,22 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
     const int qk = hs * Hk + kh, vh = 2 * Hk + kh * G + hs - 2;   // both formed, one kept
     return (hs < 2 ? qk : vh) * 128 + (c & 127);
   };
+  if (len <= 0) {
+    // no tokens: the final states are the initial ones, zero without a flag
+    if (!init) {
+      if (commit_state) store_zero_state(state + ((int64_t)s * Hv + h) * (128 * 128), v0, r16, kg);
+      if (write_conv_state && wave == 0 && (lane >> 4) < 2 + G) {
+        const int cg = chan((lane >> 4) * 128 + 8 * (lane & 15));
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          float* p = cs + (int64_t)r * C + cg;
+          *reinterpret_cast<float4*>(p) = make_float4(0.f, 0.f, 0.f, 0.f);
+          *reinterpret_cast<float4*>(p + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+    return;
+  }
 
   // staged pieces: x rows of block c0 (rows before the sequence read as
   // zeros), and the stored rows for the first block (zeros without an

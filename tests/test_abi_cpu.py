@@ -79,7 +79,7 @@ def test_host_make_chunks_bit_exact_and_capacity_is_a_bound(seed):
     r = np.random.default_rng(seed)
     lengths = r.integers(0, 400, int(r.integers(1, 40)))
     cu = np.concatenate([[0], np.cumsum(lengths)])
-    M = int(r.choice([3, 16, 64, 100]))
+    M = int(r.choice([3, 16, 63, 64]))
     n, out, bound = _make_chunks(cu, M)
     ref = O.make_chunks(cu, M)
     assert n == len(ref) <= bound
@@ -95,6 +95,27 @@ def test_host_make_chunks_errors():
     assert n == -SHAPE
     lib.gdn_make_chunks.argtypes = [vp, i32, i32, vp, i32]
     assert lib.gdn_make_chunks(None, 1, 64, None, 4) == -NULL
+
+
+@pytest.mark.parametrize("chunk_len", [-1, 0, 1, 2, 65, 100, 128])
+def test_chunk_len_outside_3_to_64_is_rejected(chunk_len):
+    # The conv kernels cover at most 64 tokens per descriptor and a
+    # non-first chunk reads its 3-row halo from its own sequence: every
+    # builder refuses other lengths before touching memory or the GPU.
+    n, _, bound = _make_chunks([0, 200, 201], chunk_len)
+    assert n == -SHAPE and bound == 0
+    dev = lib.gdn_make_chunks_device
+    dev.restype = i32
+    dev.argtypes = [vp, i32, i32, vp, i32, vp]
+    assert dev(FAKE, 2, chunk_len, FAKE + (1 << 24), 8, None) == -SHAPE
+    assert dev(FAKE, 2, chunk_len, FAKE + (1 << 24), 0, None) == -SHAPE
+
+
+@pytest.mark.parametrize("chunk_len", [3, 4, 64])
+def test_chunk_len_bounds_are_accepted(chunk_len):
+    n, out, bound = _make_chunks([0, 200, 201, 201], chunk_len)
+    ref = O.make_chunks([0, 200, 201, 201], chunk_len)
+    assert n == len(ref) <= bound and np.array_equal(out[:n], ref)
 
 
 FAKE = 0x10000000          # 16-byte aligned dummy address; never dereferenced
@@ -132,7 +153,7 @@ def test_conv_validation():
 
     def call(**kw):
         a = list(args)
-        idx = {"x": 0, "xs": 1, "act": 2, "C": 12, "y": 14, "w": 3, "N": 11}
+        idx = {"x": 0, "xs": 1, "act": 2, "C": 12, "y": 14, "w": 3, "N": 11, "ws": 13, "cs": 5}
         for k_, v_ in kw.items():
             a[idx[k_]] = v_
         return fn(*a)
@@ -143,7 +164,11 @@ def test_conv_validation():
     assert call(w=None) == NULL
     assert call(x=FAKE + 2) == ALIGN
     assert call(y=FAKE + 1024) == ALIAS
-    assert call(N=0) == OK
+    # no tokens and no final rows to write: nothing to do, no launch
+    assert call(N=0, ws=0) == OK
+    # no tokens but final rows to write (empty sequences are cleared): the
+    # state buffer is still required
+    assert call(N=0, cs=None) == NULL
 
 
 def test_recurrence_validation():
@@ -276,7 +301,8 @@ def test_decode_fused_validation():
     assert call(ko=FAKE + (8 << 24) + 256) == ALIAS   # k_out inside o
     assert call(vo=FAKE + (9 << 24), ko=FAKE + (9 << 24) + 4096) == ALIAS   # k_out inside v_out
     assert call(vo=FAKE + 128) == ALIAS     # v_out inside x
-    assert call(N=0) == OK                 # empty: no launch
+    assert call(N=0, wcs=0, commit=0) == OK   # no tokens, no final state: no launch
+    assert call(N=0, x=None, o=None, g=None, beta=None, st=None) == NULL   # zero states still need state
     assert call(nseq=0) == OK
 
 
