@@ -1,47 +1,58 @@
 """GDN layer hot-path benchmark on one MI355X.
 
-Default workload (the headline metric): the bf16 varlen prefill.  One step
-is one pass of the whole hot path over one batch: exact 64-token conv chunks
-(derived from cu_seqlens inside the conv launch; --chunk-descriptors runs
-the descriptor builder instead), causal conv with the conv_state update and
-post-conv (SiLU, split, L2) in one launch, and the chunked delta-rule
-prefill with the state update, on 8
-sequences with lengths uniform in [128, 2048], 8192 packed channels = 16 q
-+ 16 k heads and 32 v heads of 128, half of the sequences with initial
-states.  Inputs are synthetic and seeded, resident in HBM before timing
-starts.
+Default workload (the headline metric): the mixed serving step at
+concurrency 32, the largest of the five workloads that fits one GPU.  Each
+of 24 layers takes 8 prefill sequences (lengths log-uniform in [256, 8192],
+16,333 tokens) and 24 single-token decode sequences, 6144 packed channels
+(16 q, 16 k, 16 v heads of 128), bf16 activations, float32 states, all with
+initial states.  One step is one pass of the hot path over all 24 layers;
+per layer:
+  main stream  conv + post-conv of the prefill tokens in one launch (exact
+               64-token chunks derived in the launch, conv_state updated),
+               then the chunked delta-rule prefill (state updated);
+  side stream  the decode tokens' conv, post-conv and committing step in
+               one fused launch, started after the layer's conv + post-conv
+               and joined before the next layer, so it runs beside the
+               prefill (the two touch disjoint sequences).
+--serial runs every launch on one stream.  Inputs are synthetic and
+seeded, resident in HBM before timing starts.
 
-Prints ONE JSON line: throughput in tokens/s, the roofline of the dominant
-kernel (per-launch HIP-event time of each kernel inside the timed region),
-the CPU oracle timed on a bounded sample of the same workload, and a
-cold-cache pass (`cold_cache`: up to 20 more steps, each after a 1 GiB read
-that evicts L2 and the Infinity Cache, timed with events; context beside
-`value`, which is the warm timed region).
+Prints ONE JSON line: throughput in layer-tokens/s, the roofline of the
+dominant kernel (per-launch HIP-event time of each kernel inside the timed
+region, on the stream it runs on), the CPU oracle timed on a bounded sample
+of the same workload over a pool of host processes, and a cold-cache pass
+(`cold_cache`: up to 20 more steps, each after a 1 GiB read that evicts L2
+and the Infinity Cache, timed with events; context beside `value`, which is
+the warm timed region).
 
-Other workloads (--workload), each one JSON line with per-kernel stages and
-the dominant kernel's roofline, throughput in layer-tokens/s:
+Other workloads (--workload), each one JSON line in the same form:
+  varlen  the bf16 varlen prefill: 8 sequences with lengths uniform in
+          [128, 2048], 8192 channels (16 q, 16 k, 32 v heads), half with
+          initial states; conv + post-conv, then the prefill
   verify  speculative verify: 36 layers of conv shift + post-conv + decode
           step (no state write), then one batched commit of n_keep tokens
           (32 sequences, 1..8 draft tokens each)
   long    one 32768-token prefill layer
-  mixed   24 layers of a serving step: 8 prefill sequences (log-uniform
-          lengths in [256, 8192]) and 24 single-token decode sequences,
-          6144 channels (16 q, 16 k, 16 v heads)
-  verify-fused, mixed-fused
-          the same, with the decode / draft tokens' conv, post-conv and
-          step in one fused launch per layer
+  mixed-unfused
+          the mixed serving step with the decode tokens in the conv +
+          post-conv launch and a separate step launch
+  verify-fused
+          verify with each layer's conv, post-conv and step in one launch
   out-norm
           the gated output norm on the mixed serving step's o, 24 layers
   gates   the gate computation for the mixed serving step, 24 layers
+  long-seg
+          the 32768-token prefill split into 4 segments
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                  [--workload varlen|verify|long|mixed|verify-fused|mixed-fused|out-norm|gates]
+                  [--serial] [--workload mixed|varlen|verify|...]
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import multiprocessing
 import os
 import sys
 import time
@@ -52,7 +63,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFS = 2500.0
 METRIC = "GDN layer tokens/s (conv+postconv+delta-rule) and % of HBM roofline, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_varlen_prefill_bf16.json")
+# calibrated FETCH_SIZE / WRITE_SIZE traffic per kernel, one file per workload
+TRAFFIC_FILES = {"varlen": os.path.join(ROOT, "profiles", "traffic_varlen_prefill_bf16.json"),
+                 "mixed": os.path.join(ROOT, "profiles", "traffic_mixed_serving_24L_bf16.json")}
+CPU_POOL_MAX = 16          # host processes for the CPU baseline (one GPU's share of the box)
 KERNEL_SOURCES = {
     "conv": ["conv.hip", "device_common.hpp"],
     "convpost": ["conv.hip", "device_common.hpp"],
@@ -158,40 +172,103 @@ def prefill_flops(lb) -> float:
     return 11.0 * 128 * 128 * lb.N * lb.geo.Hv
 
 
-def cpu_baseline(lb) -> dict:
-    """The oracle (unchanged) on the same batch: conv, post-conv and the
-    per-token recurrence for every token and head, single-threaded float64
-    numpy.  The whole varlen batch is about 10 s of CPU work, so the sample
-    is the full workload."""
+# ------------------------------------------------------------ CPU baseline
+# The oracle, unchanged, on one layer of the workload, spread over a pool of
+# host processes.  The conv is depthwise and every group of k-heads with
+# their v-heads is independent of the others, so a unit of work is a run of
+# sequences and a group of heads: the oracle's conv, post-conv and per-token
+# recurrence on that group's channels.  Units are handed out longest first.
+
+_CPU = {}    # one layer's inputs (numpy), shared with forked workers
+
+
+def _cpu_unit(unit):
     import numpy as np
     from oracle import gdn_oracle as O
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:                              # pragma: no cover
-        limiter = None
-    cu = lb.cu_seqlens.tolist()
-    x = lb.x.float().numpy().astype(np.float64)
-    w = lb.conv_w.numpy().astype(np.float64)
-    cs = lb.conv_state.numpy().astype(np.float64)
-    st = lb.state.numpy().astype(np.float64)
-    g = lb.g.numpy().astype(np.float64)
-    b = lb.beta.numpy().astype(np.float64)
-    hi = lb.has_init.numpy()
-    Hk, Hv = lb.geo.Hk, lb.geo.Hv
+        pass
+    s0, s1, kh0, nk = unit
+    d = _CPU
+    Hk, Hv, act = d["Hk"], d["Hv"], d["act"]
+    G = Hv // Hk
+    cu = d["cu"]
+    b, e = int(cu[s0]), int(cu[s1])
+    cu_l = [int(c) - b for c in cu[s0:s1 + 1]]
+    qk = np.arange(kh0 * 128, (kh0 + nk) * 128)
+    chans = np.concatenate([qk, Hk * 128 + qk, 2 * Hk * 128 + np.arange(kh0 * G * 128, (kh0 + nk) * G * 128)])
+    heads = np.arange(kh0 * G, (kh0 + nk) * G)
+    hi = d["hi"][s0:s1]
+    y, _ = O.causal_conv(d["x"][b:e][:, chans].astype(np.float64), d["w"][chans], None,
+                         d["cs"][s0:s1][:, :, chans], hi, cu_l, True)
+    q, k, v = O.postconv_l2(O.round_to(y, act), nk, nk * G, 128, 128, 1e-6)
+    q, k, v = (O.round_to(a, act) for a in (q, k, v))
+    o, _ = O.delta_rule_recurrent(q, k, v, d["g"][b:e][:, heads], d["beta"][b:e][:, heads],
+                                  d["st"][s0:s1][:, heads], hi, cu_l, nk, nk * G)
+    return float(np.abs(o).sum())
+
+
+def _cpu_units(cu, Hk, head_groups=4, min_tokens=256):
+    """Runs of consecutive sequences of at least min_tokens tokens (a long
+    sequence alone), times head_groups groups of k-heads; longest first."""
+    runs, s0 = [], 0
+    nseq = len(cu) - 1
+    for s in range(nseq):
+        if cu[s + 1] - cu[s0] >= min_tokens or s == nseq - 1:
+            runs.append((s0, s + 1))
+            s0 = s + 1
+    nk = max(1, Hk // head_groups)
+    units = [(a, b, kh, min(nk, Hk - kh)) for a, b in runs for kh in range(0, Hk, nk)]
+    return sorted(units, key=lambda u: -(cu[u[1]] - cu[u[0]]))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(lb, layers: int) -> dict:
+    """The oracle on one layer's whole batch (every sequence, every head),
+    over min(16, cpu_count) processes forked before the GPU is touched.
+    Result in tokens/s of that layer, the metric's unit (layer-tokens/s)."""
+    import numpy as np
+    import torch
+    _CPU.clear()
+    _CPU.update(x=lb.x.float().numpy(), w=lb.conv_w.numpy().astype(np.float64),
+                cs=lb.conv_state.numpy().astype(np.float64), st=lb.state.numpy().astype(np.float64),
+                g=lb.g.numpy().astype(np.float64), beta=lb.beta.numpy().astype(np.float64),
+                hi=lb.has_init.numpy(), cu=lb.cu_seqlens.numpy().astype(np.int64),
+                Hk=lb.geo.Hk, Hv=lb.geo.Hv, act=lb.act)
+    units = _cpu_units(_CPU["cu"], lb.geo.Hk)
+    nproc = os.cpu_count() or 1
+    workers = min(CPU_POOL_MAX, nproc, len(units))
+    if torch.cuda.is_initialized():
+        workers = 1          # never fork a process that holds the GPU
     t0 = time.perf_counter()
-    y, _ = O.causal_conv(x, w, None, cs, hi, cu, True)
-    q, k, v = O.postconv_l2(O.round_to_bf16(y), Hk, Hv, 128, 128, 1e-6)
-    del y
-    q, k, v = O.round_to_bf16(q), O.round_to_bf16(k), O.round_to_bf16(v)
-    O.delta_rule_recurrent(q, k, v, g, b, st, hi, cu, Hk, Hv)
-    dt = time.perf_counter() - t0
-    if limiter is not None and hasattr(limiter, "unregister"):
-        limiter.unregister()
-    return {"value": lb.N / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full batch ({lb.nseq} sequences, {lb.N} tokens): conv, post-conv "
-                      f"and per-token recurrence over all {Hv} v-heads, float64 numpy, one thread",
-            "seconds": round(dt, 2)}
+    if workers > 1:
+        with multiprocessing.get_context("fork").Pool(workers) as pool:
+            t0 = time.perf_counter()
+            list(pool.imap_unordered(_cpu_unit, units, chunksize=1))
+            dt = time.perf_counter() - t0
+    else:
+        for u in units:
+            _cpu_unit(u)
+        dt = time.perf_counter() - t0
+    _CPU.clear()
+    return {"value": round(lb.N / dt, 1), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"one of the {layers} layers: all {lb.nseq} sequences ({lb.N} tokens) and all "
+                      f"{lb.geo.Hv} v-heads through the oracle's conv, post-conv and per-token "
+                      f"recurrence (float64 numpy), {len(units)} units (a run of sequences x 4 of the "
+                      f"{lb.geo.Hk} k-heads with their v-heads) over {workers} host processes",
+            "seconds": round(dt, 2), "nproc": nproc, "cpu_model": cpu_model()}
 
 
 # ------------------------------------------------------------------ workloads
@@ -200,8 +277,12 @@ def cpu_baseline(lb) -> dict:
 # one step and the config dict.
 
 class Plan:
+    """The ordered launches of one step.  ops: ("run", name, fn, stream),
+    ("mark", key, stream) records an event on a stream, ("wait", key,
+    stream) makes a stream wait for it; stream 0 is the caller's stream."""
+
     def __init__(self):
-        self.launches = []       # (kernel name, callable)
+        self.ops = []
         self.bytes = {}          # kernel name -> bytes per step
         self.count = {}          # kernel name -> launches per step
         self.flops = {}          # kernel name -> dense flops per step
@@ -209,13 +290,72 @@ class Plan:
         self.dtype = "bf16"      # arithmetic type of the step's activations
         self.config = {}
         self.keep = []           # tensors kept alive
+        self.lb = None           # one layer's inputs (CPU), for the CPU baseline
 
-    def add(self, name, fn, nbytes, flops=0.0):
-        self.launches.append((name, fn))
+    def add(self, name, fn, nbytes, flops=0.0, stream=0):
+        self.ops.append(("run", name, fn, stream))
         self.bytes[name] = self.bytes.get(name, 0) + nbytes
         self.count[name] = self.count.get(name, 0) + 1
         if flops:
             self.flops[name] = self.flops.get(name, 0.0) + flops
+
+    def mark(self, key, stream=0):
+        self.ops.append(("mark", key, stream))
+
+    def wait(self, key, stream=0):
+        self.ops.append(("wait", key, stream))
+
+    @property
+    def launches(self):
+        return [(op[1], op[2]) for op in self.ops if op[0] == "run"]
+
+
+class Runner:
+    """Issues a plan's ops on the caller's stream and side streams (default
+    priority), optionally bracketing every launch with HIP events on the
+    stream it runs on.  serial=True puts everything on the caller's stream."""
+
+    def __init__(self, plan, stream, serial=False):
+        import torch
+        self.plan = plan
+        self.serial = serial
+        n = 1 if serial else 1 + max([op[3] if op[0] == "run" else op[2] for op in plan.ops], default=0)
+        self.streams = [stream] + [torch.cuda.Stream(device=stream.device) for _ in range(n - 1)]
+        self.marks = {op[1]: torch.cuda.Event() for op in plan.ops if op[0] == "mark"}
+        self.n_runs = sum(1 for op in plan.ops if op[0] == "run")
+
+    def events(self):
+        import torch
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(self.n_runs)]
+
+    def step(self, ev=None):
+        import torch
+        i = 0
+        for op in self.plan.ops:
+            if op[0] == "run":
+                st = self.streams[0 if self.serial else op[3]]
+                with torch.cuda.stream(st):
+                    if ev is not None:
+                        ev[i][0].record(st)
+                    op[2]()
+                    if ev is not None:
+                        ev[i][1].record(st)
+                i += 1
+            elif self.serial:
+                continue
+            elif op[0] == "mark":
+                self.marks[op[1]].record(self.streams[op[2]])
+            else:
+                self.streams[op[2]].wait_event(self.marks[op[1]])
+
+    def stage_ms(self, ev):
+        """Per-kernel-name milliseconds of one step from its event pairs."""
+        out = {}
+        names = [nm for nm, _ in self.plan.launches]
+        for nm, (a, b) in zip(names, ev):
+            out[nm] = out.get(nm, 0.0) + a.elapsed_time(b)
+        return out
 
 
 def _layer_on_device(lb, dev):
@@ -341,12 +481,19 @@ def plan_long(dev, nseg=1):
     return p
 
 
-def plan_mixed(dev, fused=False):
+def plan_mixed(dev, fused=True):
+    """24 layers of the mixed serving step.  Per layer the decode tokens'
+    launch (fused conv + post-conv + step, or the step alone after a conv +
+    post-conv over all tokens when not fused) goes to side stream 1 once the
+    layer's conv + post-conv is done, and stream 0 waits for it before the
+    next layer: it runs beside the prefill, which touches other sequences."""
     from linear_attention_layers_amd import gdn, inputs
     L = 24
     p = Plan()
     for layer in range(L):
         lb = inputs.mixed_serving_layer(layer)
+        if layer == 0:
+            p.lb = lb
         d = _layer_on_device(lb, dev)
         npre = lb.meta["n_prefill"]
         Npre = int(lb.cu_seqlens[npre])
@@ -367,6 +514,8 @@ def plan_mixed(dev, fused=False):
             add_conv_post(p, d["x"], d["w"], d["cs"], None, d["cu"], d["chunks"] if descriptors_needed() else None,
                           True, Hk, Hv, N, C,
                           lb.nseq, lb.nseq, d["y"], d["q"], d["k"], d["v"])
+        p.mark(f"conv{layer}", 0)
+        p.wait(f"conv{layer}", 1)
         p.add("prefill", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_prefill(
                   d["q"][:n], d["k"][:n], d["v"][:n], d["g"][:n], d["beta"][:n], d["cu_pre"],
                   d["st"][:m], None, o=d["o"][:n]),
@@ -376,18 +525,21 @@ def plan_mixed(dev, fused=False):
                       d["x"][n:], d["w"], None, d["cs"][m:], d["cu_dec"], d["g"][n:], d["beta"][n:],
                       d["st"][m:], Hk, Hv, 1e-6, None, o=d["o"][n:], write_conv_state=True,
                       commit_state=True),
-                  fused_bytes(N - Npre, C, Hk, Hv, 2, ndec, True, ndec, False))
+                  fused_bytes(N - Npre, C, Hk, Hv, 2, ndec, True, ndec, False), stream=1)
         else:
             p.add("step", lambda d=d, n=Npre, m=npre: gdn.gdn_delta_rule_step(
                       d["q"][n:], d["k"][n:], d["v"][n:], d["g"][n:], d["beta"][n:], d["cu_dec"],
                       d["st"][m:], None, o=d["o"][n:], commit_state=True),
-                  recurrence_bytes(N - Npre, Hk, Hv, 2, ndec, ndec))
+                  recurrence_bytes(N - Npre, Hk, Hv, 2, ndec, ndec), stream=1)
+        p.mark(f"dec{layer}", 1)
+        p.wait(f"dec{layer}", 0)
         p.keep.append(d)
         p.tokens += N
-        p.config = {"workload": "mixed_serving_24L_bf16" + ("_fused" if fused else ""),
+        p.config = {"workload": "mixed_serving_24L_bf16" + ("" if fused else "_unfused"),
                     "prefill_seqs": npre, "decode_seqs": ndec,
                     "tokens_per_layer": N, "channels": C, "Hk": Hk, "Hv": Hv, "head_dim": 128,
-                    "layers": L, "state_dtype": "f32", "seed": 5000}
+                    "layers": L, "state_dtype": "f32", "seed": 5000,
+                    "decode": ("fused conv + post-conv + step" if fused else "step") + " on a side stream"}
     return p
 
 
@@ -444,31 +596,46 @@ def plan_gates(dev):
 
 PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed,
          "verify-fused": lambda dev: plan_verify(dev, fused=True),
-         "mixed-fused": lambda dev: plan_mixed(dev, fused=True), "out-norm": plan_out_norm,
+         "mixed-unfused": lambda dev: plan_mixed(dev, fused=False), "out-norm": plan_out_norm,
          "gates": plan_gates, "long-seg": lambda dev: plan_long(dev, nseg=4)}
 
 
-def cold_pass(plan, stream, reps):
+def cpu_sample(workload):
+    """(one layer's inputs on the CPU, layers in the workload) for the CPU
+    baseline, or None where the workload has no baseline leg."""
+    from linear_attention_layers_amd import inputs
+    if workload == "varlen":
+        return inputs.varlen_prefill(), 1
+    if workload == "mixed":
+        return inputs.mixed_serving_layer(0), 24
+    return None
+
+
+def cold_pass(runner, reps):
     """Each of `reps` steps runs right after a 1 GiB read of an unrelated
     buffer (clean lines: it evicts L2 and the Infinity Cache without leaving
-    write-backs behind), with HIP events on the launch stream around every
-    kernel and around the step; the read itself is outside the events."""
+    write-backs behind), with HIP events around every kernel and around the
+    step; the read itself is outside the events."""
     import torch
-    scratch = torch.ones(1 << 28, dtype=torch.float32, device=stream.device)
+    plan = runner.plan
+    main = runner.streams[0]
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=main.device)
     names = list(dict.fromkeys(nm for nm, _ in plan.launches))
     acc = {nm: 0.0 for nm in names}
     total = 0.0
     for _ in range(reps):
         scratch.sum()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan.launches) + 1)]
-        ev[0].record(stream)
-        for i, (_, fn) in enumerate(plan.launches):
-            fn()
-            ev[i + 1].record(stream)
+        ev = runner.events()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(main)
+        runner.step(ev)
+        for st in runner.streams[1:]:
+            main.wait_stream(st)
+        t1.record(main)
         torch.cuda.synchronize()
-        for j, (nm, _) in enumerate(plan.launches):
-            acc[nm] += ev[j].elapsed_time(ev[j + 1])
-        total += ev[0].elapsed_time(ev[-1])
+        for nm, ms in runner.stage_ms(ev).items():
+            acc[nm] += ms
+        total += t0.elapsed_time(t1)
     del scratch
     stages = {}
     for nm in names:
@@ -486,8 +653,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", choices=sorted(PLANS), default="varlen")
+    ap.add_argument("--workload", choices=sorted(PLANS), default="mixed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="issue every launch on one stream (no side stream for the decode tokens)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (steps run after a 1 GiB read that evicts L2 and the "
                          "256 MB Infinity Cache; reported beside the timed region, never as value)")
@@ -505,12 +674,20 @@ def main():
               "(the GDN hot path shards by sequence and head group with no exchange; "
               "multi-GPU runs are not part of this build)", file=sys.stderr)
         sys.exit(2)
-    default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 10, "verify-fused": 20,
-                     "mixed-fused": 10, "out-norm": 20, "gates": 20, "long-seg": 20}[args.workload]
+    default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 40, "verify-fused": 20,
+                     "mixed-unfused": 20, "out-norm": 20, "gates": 20, "long-seg": 20}[args.workload]
     steps = args.steps if args.steps is not None else default_steps
     warmup = args.warmup if args.warmup is not None else max(2, steps // 10)
 
     import torch
+
+    # the CPU baseline runs first: its worker processes are forked before
+    # this process touches the GPU
+    cpu = None
+    sample = None if args.no_cpu_baseline or args.copy_calibration else cpu_sample(args.workload)
+    if sample is not None:
+        cpu = cpu_baseline(*sample)
+        del sample
 
     dev = torch.device("cuda", 0)
     if args.copy_calibration:
@@ -530,33 +707,25 @@ def main():
     CHUNK_DESCRIPTORS = args.chunk_descriptors
     plan = PLANS[args.workload](dev)
     stream = torch.cuda.current_stream()
-    n_l = len(plan.launches)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        for i, (_, fn) in enumerate(plan.launches):
-            fn()
-            if ev is not None:
-                ev[i + 1].record(stream)
+    runner = Runner(plan, stream, serial=args.serial)
 
     for _ in range(warmup):
-        step()
+        runner.step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_l + 1)] for _ in range(steps)]
+    events = [runner.events() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        runner.step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     names = list(dict.fromkeys(nm for nm, _ in plan.launches))
     per_step_ms = {nm: 0.0 for nm in names}
     for ev in events:
-        for j, (nm, _) in enumerate(plan.launches):
-            per_step_ms[nm] += ev[j].elapsed_time(ev[j + 1])
+        for nm, ms in runner.stage_ms(ev).items():
+            per_step_ms[nm] += ms
     per_step_ms = {nm: t / steps for nm, t in per_step_ms.items()}
 
     ms_per_step = wall * 1e3 / steps
@@ -579,18 +748,23 @@ def main():
     achieved = plan.bytes[dominant] / (per_step_ms[dominant] / 1e3) / 1e9
 
     traffic = None
-    if args.workload == "varlen":
+    if args.workload in TRAFFIC_FILES and not (args.split_conv or args.chunk_descriptors or args.serial):
         try:
-            with open(TRAFFIC_FILE) as f:
+            with open(TRAFFIC_FILES[args.workload]) as f:
                 rec = json.load(f).get(dominant)
             if rec and rec.get("source_hash") == source_hash(dominant):
                 traffic = rec["bytes_per_launch"]
         except (OSError, ValueError):
             pass
 
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": plan.bytes[dominant] // plan.count[dominant]}
+    if plan.flops.get(dominant):
+        # the chunked prefill's dense contractions against the bf16 MFMA peak
+        roofline["mfma_frac"] = stages[dominant]["mfma_frac_bf16_dense"]
     out = {
-        "metric": METRIC if args.workload == "varlen" else
-        f"GDN {args.workload} step layer-tokens/s and % of HBM roofline, 1 GPU",
+        "metric": METRIC,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -603,16 +777,13 @@ def main():
         "dtype": plan.dtype,
         "data": "synthetic",
         "config": plan.config,
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "algorithmic_bytes": plan.bytes[dominant] // plan.count[dominant]},
+        "roofline": roofline,
         "stages": stages,
     }
     if not args.no_cold:
-        out["cold_cache"] = cold_pass(plan, stream, min(steps, 20))
-    if args.workload == "varlen" and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(plan.lb)
+        out["cold_cache"] = cold_pass(runner, min(steps, 20))
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -95,6 +95,22 @@ template <> struct Prec<uint16_t> {
                      pack_bf16x2(d1[2], d1[3]));
     return f;
   }
+  // The float32 operand split in two bf16 operands, hi = bf16(x) (reg32's
+  // result) and lo = bf16(x - hi): hi + lo carries 16 significant bits, so a
+  // product taken as hi * B + lo * B has the operand's rounding error near
+  // 2^-17 instead of 2^-9.  x - hi is exact in float32.
+  __device__ __forceinline__ static F32 reg32_lo(f32x4 d0, f32x4 d1, F32 hi) {
+    const unsigned h[4] = {hi.v.x, hi.v.y, hi.v.z, hi.v.w};
+    const float x[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+    unsigned lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lo[i] = pack_bf16x2(x[2 * i] - __uint_as_float(h[i] << 16), x[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
+    F32 f;
+    f.v = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    return f;
+  }
+  static constexpr bool kSplitState = true;
   __device__ __forceinline__ static f32x4 mma16(F16 a, F16 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v),
                                                      __builtin_bit_cast(s16x4, b.v), c, 0, 0, 0);
@@ -177,6 +193,9 @@ template <> struct Prec<float> {
   }
   __device__ __forceinline__ static F16 reg16(f32x4 d) { F16 f; f.v = d; return f; }
   __device__ __forceinline__ static F32 reg32(f32x4 d0, f32x4 d1) { F32 f; f.a = d0; f.b = d1; return f; }
+  // float32 operands are exact: no second part
+  __device__ __forceinline__ static F32 reg32_lo(f32x4, f32x4, F32 hi) { return hi; }
+  static constexpr bool kSplitState = false;
   // slot t of lane kg is contraction index 4kg + t: four k = 4 steps
   __device__ __forceinline__ static f32x4 mma4x(f32x4 a, f32x4 b, f32x4 c) {
 #pragma unroll

@@ -251,7 +251,11 @@ __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Pre
   }
   const auto tf = PR::lds16(Tm, LDT, r16, 0, kg);
 
-  // Z = K S0^T (rows: tokens) and (Q S0^T)^T (rows: state rows)
+  // Z = K S0^T (rows: tokens) and (Q S0^T)^T (rows: state rows).  With bf16
+  // operands the float32 state enters as hi + lo (two products each): one
+  // bf16 rounding of S0 here, taken at every call, costs the outputs and the
+  // deltas (v - a S0 k cancels as the rule converges) about 2^-9 of |S0|
+  // per token, which a chain of one-token decode steps never averages out.
   f32x4 z[kRB], qt[kRB];
 #pragma unroll
   for (int b = 0; b < kRB; ++b) { z[b] = zero4(); qt[b] = zero4(); }
@@ -265,6 +269,11 @@ __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Pre
       const auto bs = PR::reg32(st[b][2 * t], st[b][2 * t + 1]);
       z[b] = PR::mma32(kf, bs, z[b]);
       if (WITH_O) qt[b] = PR::mma32(bs, qf, qt[b]);
+      if constexpr (PR::kSplitState) {
+        const auto bl = PR::reg32_lo(st[b][2 * t], st[b][2 * t + 1], bs);
+        z[b] = PR::mma32(kf, bl, z[b]);
+        if (WITH_O) qt[b] = PR::mma32(bl, qf, qt[b]);
+      }
     }
   }
 

@@ -45,3 +45,47 @@ def test_commit_byte_model_skips_sequences_that_keep_nothing():
     tokens = 3 * (16 * 128 + 32 * 128) * 2 + 3 * 32 * 8 + 3 * 8192 * 2
     conv_rows = 24 * 8192
     assert got == state + tokens + conv_rows
+
+
+def test_cpu_baseline_units_cover_every_sequence_and_head_once():
+    import numpy as np
+    for lengths, Hk in ((I.mixed_lengths(), 16), (I.varlen_lengths(), 16), ([1] * 5, 2), ([300], 16),
+                        ([0, 7, 0, 400, 3], 4)):
+        cu = np.concatenate([[0], np.cumsum(lengths)])
+        cover = np.zeros((len(lengths), Hk), dtype=int)
+        for s0, s1, kh0, nk in bench._cpu_units(cu, Hk):
+            cover[s0:s1, kh0:kh0 + nk] += 1
+        assert (cover == 1).all(), (lengths, Hk)
+
+
+def test_cpu_baseline_units_compute_the_whole_layer():
+    # the per-unit oracle runs (a run of sequences x a group of heads, on that
+    # group's channels) add up to the oracle on the whole batch
+    import numpy as np
+    from oracle import gdn_oracle as O
+    lb = I.make_layer(I.Geometry(Hk=2, Hv=4), [70, 1, 1, 300], "bf16", 77, state_std=0.3,
+                      has_init=[1, 0, 1, 1])
+    bench._CPU.clear()
+    bench._CPU.update(x=lb.x.float().numpy(), w=lb.conv_w.numpy().astype(np.float64),
+                      cs=lb.conv_state.numpy().astype(np.float64), st=lb.state.numpy().astype(np.float64),
+                      g=lb.g.numpy().astype(np.float64), beta=lb.beta.numpy().astype(np.float64),
+                      hi=lb.has_init.numpy(), cu=lb.cu_seqlens.numpy().astype(np.int64), Hk=2, Hv=4, act="bf16")
+    units = bench._cpu_units(bench._CPU["cu"], 2, min_tokens=64)
+    assert len(units) > 2
+    total = sum(bench._cpu_unit(u) for u in units)
+    bench._CPU.clear()
+    cu = lb.cu_seqlens.tolist()
+    y, _ = O.causal_conv(lb.x.float().numpy().astype(np.float64), lb.conv_w.numpy(), None,
+                         lb.conv_state.numpy(), lb.has_init.numpy(), cu, True)
+    q, k, v = (O.round_to_bf16(a) for a in O.postconv_l2(O.round_to_bf16(y), 2, 4, 128, 128, 1e-6))
+    o, _ = O.delta_rule_recurrent(q, k, v, lb.g.numpy(), lb.beta.numpy(), lb.state.numpy(),
+                                  lb.has_init.numpy(), cu, 2, 4)
+    assert abs(total - float(np.abs(o).sum())) <= 1e-9 * float(np.abs(o).sum())
+
+
+def test_default_workload_is_the_mixed_serving_step():
+    import argparse  # noqa: F401
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--workload", choices=sorted(PLANS), default="mixed")' in src
+    lb, layers = bench.cpu_sample("mixed")
+    assert layers == 24 and lb.geo.C == 6144 and lb.nseq == 32 and lb.N == sum(I.mixed_lengths())
