@@ -271,6 +271,31 @@ int gdn_delta_rule_prefill_segmented(const void* q, const void* k, const void* v
                                      void* o, int nseg, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* ---- 4c. segment-parallel prefill without allocation ------------------------
+ * For callers that cannot allocate device memory around the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * gdn_delta_rule_prefill_segmented with the workspace taken from a scratch
+ * array inside the library (GDN_NOALLOC_SCRATCH_BYTES per GPU, held until
+ * the process ends) instead of the caller's buffer; no hipMalloc, hipFree or
+ * other allocating call is made.  Same arguments and results (bitwise) as
+ * item 4b minus the workspace.
+ *   - gdn_prefill_segmented_workspace(nseq, Hv, nseg) must not exceed
+ *     GDN_NOALLOC_SCRATCH_BYTES (GDN_ERR_CAPACITY otherwise, before any
+ *     launch); e.g. one sequence with Hv = 32 and nseg = 4 takes 24 MiB.
+ *   - Every call on a GPU shares that GPU's scratch, which keeps the last
+ *     call's X, R and P (nothing in it needs to start at zero): calls that
+ *     overlap on one GPU (several streams, several host threads) race.
+ *     Issue them on one stream, or use item 4b with separate workspaces.
+ *   - The scratch address is looked up once per device, on the first call
+ *     for the stream's device; a failure there is GDN_ERR_LAUNCH. */
+#define GDN_NOALLOC_SCRATCH_BYTES (24u << 20)
+int gdn_delta_rule_prefill_segmented_noalloc(const void* q, const void* k, const void* v, int act,
+                                             const float* g, const float* beta,
+                                             const int32_t* cu_seqlens, int nseq, int N,
+                                             int Hk, int Hv, int dk, int dv,
+                                             float* state, const uint8_t* has_initial_state,
+                                             void* o, int nseg, void* stream);
+
 /* ---- 5. decode / verify step ---------------------------------------------
  * The same recurrence token by token with the state held in registers
  * ("Summary" item 3: state-resident per-token step).  Every sequence's

@@ -272,6 +272,29 @@ int gdn_delta_rule_prefill_segmented(const void* q, const void* k, const void* v
                   "delta_rule_prefill_segmented");
 }
 
+int gdn_delta_rule_prefill_segmented_noalloc(const void* q, const void* k, const void* v, int act,
+                                             const float* g, const float* beta, const int32_t* cu,
+                                             int nseq, int N, int Hk, int Hv, int dk, int dv, float* state,
+                                             const uint8_t* has_init, void* o, int nseg, void* stream) {
+  int st = check_recurrence(q, k, v, act, g, beta, cu, nseq, N, Hk, Hv, dk, dv, state, o);
+  if (st != GDN_OK) return st;
+  if (nseg < 1 || nseg > 64) return fail(GDN_ERR_SHAPE, "nseg must be in 1..64 (got %d)", nseg);
+  if (nseg == 1) return gdn_delta_rule_prefill(q, k, v, act, g, beta, cu, nseq, N, Hk, Hv, dk, dv, state,
+                                               has_init, o, stream);
+  if (act != GDN_BF16) return fail(GDN_ERR_DTYPE, "the segmented prefill needs bf16 activations");
+  if (nseq == 0) return GDN_OK;
+  const size_t need = gdn_prefill_segmented_workspace(nseq, Hv, nseg);
+  if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ERR_CAPACITY, "nseq %d x nseg %d x Hv %d needs %zu bytes of scratch; the limit is %zu",
+                nseq, nseg, Hv, need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  float* ws = nullptr;
+  const hipError_t e = gdn::noalloc_scratch(as_stream(stream), &ws);
+  if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "scratch address: %s", hipGetErrorString(e));
+  return launched(gdn::launch_prefill_segmented(q, k, v, g, beta, cu, nseq, Hk, Hv, state, has_init, o, nseg, ws,
+                                                as_stream(stream)),
+                  "delta_rule_prefill_segmented_noalloc");
+}
+
 int gdn_delta_rule_step(const void* q, const void* k, const void* v, int act, const float* g,
                         const float* beta, const int32_t* cu, int nseq, int N, int Hk, int Hv,
                         int dk, int dv, float* state, const uint8_t* has_init, void* o,

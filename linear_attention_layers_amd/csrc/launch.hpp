@@ -52,6 +52,10 @@ hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v,
                                     const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
                                     float* state, const uint8_t* has_init, void* o, int nseg,
                                     float* ws, hipStream_t st);
+// Device address of the no-allocation scratch (GDN_NOALLOC_SCRATCH_BYTES)
+// on the stream's device (the current device for a NULL stream), looked up
+// once per device.
+hipError_t noalloc_scratch(hipStream_t st, float** out);
 hipError_t launch_prefill(const void* q, const void* k, const void* v, int act, const float* g,
                           const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,
                           float* state, const uint8_t* has_init, void* o, hipStream_t st);

@@ -40,6 +40,7 @@
 // rounded to bf16 only as an MFMA operand; the 16x16 diagonal inverses are
 // float32.  float32 activations: every contraction uses
 // v_mfma_f32_16x16x4_f32 on float32 operands.
+#include <mutex>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -1196,6 +1197,43 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const float* g,
 }
 
 }  // namespace
+
+// Device scratch of the no-allocation segmented prefill: the X, R and P
+// matrices that the allocating entry point keeps in its caller's workspace,
+// at most GDN_NOALLOC_SCRATCH_BYTES.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) float scratch[GDN_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+hipError_t noalloc_scratch(hipStream_t st, float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // once per device, with that device current
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_prefill_segmented(const void* q, const void* k, const void* v, const float* g,
                                     const float* beta, const int32_t* cu, int nseq, int Hk, int Hv,

@@ -83,6 +83,9 @@ _seg_ws = _sig("gdn_prefill_segmented_workspace", [_i32, _i32, _i32], ctypes.c_s
 _prefill_seg = _sig("gdn_delta_rule_prefill_segmented", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32,
                                                          _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
                                                          ctypes.c_size_t, _vp])
+_prefill_seg_na = _sig("gdn_delta_rule_prefill_segmented_noalloc", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
+                                                                    _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                                                    _i32, _vp])
 _step = _sig("gdn_delta_rule_step", [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _vp, _vp, _vp, _i32, _vp])
 _commit = _sig("gdn_commit", [_vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -97,7 +100,8 @@ _gates = _sig("gdn_gates", [_vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp])
 EXPORTED = ["gdn_abi_version", "gdn_status_string", "gdn_last_error", "gdn_chunk_capacity",
             "gdn_make_chunks", "gdn_make_chunks_device", "gdn_causal_conv_fwd", "gdn_conv_postconv_fwd",
             "gdn_postconv_l2", "gdn_delta_rule_prefill", "gdn_prefill_segmented_workspace",
-            "gdn_delta_rule_prefill_segmented", "gdn_delta_rule_step", "gdn_commit",
+            "gdn_delta_rule_prefill_segmented", "gdn_delta_rule_prefill_segmented_noalloc",
+            "gdn_delta_rule_step", "gdn_commit",
             "gdn_decode_fused", "gdn_out_norm", "gdn_gates"]
 
 
@@ -320,6 +324,20 @@ def gdn_delta_rule_prefill_segmented(q, k, v, g, beta, cu_seqlens, state, nseg: 
                         _ptr(cu_seqlens), nseq, N, Hk, Hv, dk, dv, _ptr(state),
                         _ptr(has_initial_state), _ptr(o), nseg, _ptr(workspace), nbytes,
                         _stream(stream)), "gdn_delta_rule_prefill_segmented")
+    return o
+
+
+def gdn_delta_rule_prefill_segmented_noalloc(q, k, v, g, beta, cu_seqlens, state, nseg: int,
+                                             has_initial_state=None, o: Optional[torch.Tensor] = None,
+                                             stream=None) -> torch.Tensor:
+    """The segmented prefill with the library's own device scratch instead
+    of a workspace (C ABI gdn_delta_rule_prefill_segmented_noalloc).  The C
+    call allocates nothing; pass o to keep this wrapper from allocating it."""
+    N, Hk, Hv, dk, dv, nseq, o = _recurrence_args(q, k, v, g, beta, cu_seqlens, state, o)
+    _check(_prefill_seg_na(_ptr(q), _ptr(k), _ptr(v), _code(q.dtype), _ptr(g), _ptr(beta),
+                           _ptr(cu_seqlens), nseq, N, Hk, Hv, dk, dv, _ptr(state),
+                           _ptr(has_initial_state), _ptr(o), nseg, _stream(stream)),
+           "gdn_delta_rule_prefill_segmented_noalloc")
     return o
 
 
