@@ -20,9 +20,10 @@ seeded, resident in HBM before timing starts.
 Prints ONE JSON line: throughput in layer-tokens/s, the roofline of the
 dominant kernel (its per-launch HIP-event time inside the timed region, on
 the stream it runs on; the warm-up steps, timed per launch, pick it), every
-kernel's time from an instrumented pass after the timed region (an event
-record between two launches costs the GPU several microseconds, so the
-timed region brackets the dominant kernel only), the CPU oracle timed on a
+kernel's time from an instrumented pass after the timed region (the timed
+region brackets the dominant kernel only; every event is created with
+hipEventDisableSystemFence, so recording one adds no cache write-back), the
+CPU oracle timed on a
 bounded sample of the same workload over a pool of host processes, and a
 cold-cache pass (`cold_cache`: up to 20 more steps, each after a 1 GiB read
 that evicts L2 and the Infinity Cache, timed with events; context beside
@@ -313,6 +314,61 @@ class Plan:
         return [(op[1], op[2]) for op in self.ops if op[0] == "run"]
 
 
+# HIP event flags (hip_runtime_api.h).  The bench's events are created with
+# hipEventDisableSystemFence: by default recording an event performs a
+# system-scope release, which writes the caches back at every record (about
+# 9 us per record after a kernel that wrote hundreds of MB, measured on the
+# mixed serving step: 5.56 against 5.24 ms per step); a timing or ordering
+# marker inside the step should not add that cost.  Work on one device stays
+# ordered and visible through the kernels' own dispatch fences.
+HIP_EVENT_DISABLE_TIMING = 0x2
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class HipEvents:
+    """hipEvent_t objects with explicit flags, through the HIP runtime that
+    torch loaded (looked up in the process's mappings, so no second runtime
+    is loaded)."""
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for ln in f:
+                if "libamdhip64" in ln:
+                    path = ln.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.ct = ctypes
+        self.lib = ctypes.CDLL(path)
+
+    def create(self, timing=True):
+        ev = self.ct.c_void_p()
+        flags = HIP_EVENT_DISABLE_SYSTEM_FENCE | (0 if timing else HIP_EVENT_DISABLE_TIMING)
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(ev), self.ct.c_uint(flags))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+        return ev
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: {rc}")
+
+    def wait(self, stream, ev):
+        rc = self.lib.hipStreamWaitEvent(self.ct.c_void_p(stream.cuda_stream), ev, self.ct.c_uint(0))
+        if rc != 0:
+            raise RuntimeError(f"hipStreamWaitEvent: {rc}")
+
+    def elapsed(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return ms.value
+
+
 class Runner:
     """Issues a plan's ops on the caller's stream and side streams (default
     priority), optionally bracketing every launch with HIP events on the
@@ -324,19 +380,16 @@ class Runner:
         self.serial = serial
         n = 1 if serial else 1 + max([op[3] if op[0] == "run" else op[2] for op in plan.ops], default=0)
         self.streams = [stream] + [torch.cuda.Stream(device=stream.device) for _ in range(n - 1)]
-        self.marks = {op[1]: torch.cuda.Event() for op in plan.ops if op[0] == "mark"}
+        self.hip = HipEvents()
+        self.marks = {op[1]: self.hip.create(timing=False) for op in plan.ops if op[0] == "mark"}
         self.n_runs = sum(1 for op in plan.ops if op[0] == "run")
 
     def events(self):
-        import torch
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(self.n_runs)]
+        return [(self.hip.create(), self.hip.create()) for _ in range(self.n_runs)]
 
     def step(self, ev=None, only=None):
         """One step; with ev, launches are bracketed by their event pair
-        (only the launches of kernel `only` when it is given: an event
-        record between two launches costs several microseconds of GPU
-        time)."""
+        (only the launches of kernel `only` when it is given)."""
         import torch
         i = 0
         for op in self.plan.ops:
@@ -345,17 +398,17 @@ class Runner:
                 timed = ev is not None and (only is None or op[1] == only)
                 with torch.cuda.stream(st):
                     if timed:
-                        ev[i][0].record(st)
+                        self.hip.record(ev[i][0], st)
                     op[2]()
                     if timed:
-                        ev[i][1].record(st)
+                        self.hip.record(ev[i][1], st)
                 i += 1
             elif self.serial:
                 continue
             elif op[0] == "mark":
-                self.marks[op[1]].record(self.streams[op[2]])
+                self.hip.record(self.marks[op[1]], self.streams[op[2]])
             else:
-                self.streams[op[2]].wait_event(self.marks[op[1]])
+                self.hip.wait(self.streams[op[2]], self.marks[op[1]])
 
     def stage_ms(self, ev, only=None):
         """Per-kernel-name milliseconds of one step from its event pairs."""
@@ -363,7 +416,7 @@ class Runner:
         names = [nm for nm, _ in self.plan.launches]
         for nm, (a, b) in zip(names, ev):
             if only is None or nm == only:
-                out[nm] = out.get(nm, 0.0) + a.elapsed_time(b)
+                out[nm] = out.get(nm, 0.0) + self.hip.elapsed(a, b)
         return out
 
     def instrumented(self, steps):
@@ -653,16 +706,16 @@ def cold_pass(runner, reps):
     for _ in range(reps):
         scratch.sum()
         ev = runner.events()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(main)
+        t0, t1 = runner.hip.create(), runner.hip.create()
+        runner.hip.record(t0, main)
         runner.step(ev)
         for st in runner.streams[1:]:
             main.wait_stream(st)
-        t1.record(main)
+        runner.hip.record(t1, main)
         torch.cuda.synchronize()
         for nm, ms in runner.stage_ms(ev).items():
             acc[nm] += ms
-        total += t0.elapsed_time(t1)
+        total += runner.hip.elapsed(t0, t1)
     del scratch
     stages = {}
     for nm in names:
