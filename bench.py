@@ -15,16 +15,22 @@ per layer:
                and joined before the next layer, so it runs beside the
                prefill (the two touch disjoint sequences).
 --serial runs every launch on one stream.  Inputs are synthetic and
-seeded, resident in HBM before timing starts.
+seeded, resident in HBM before timing starts.  The K timed steps are
+captured once as one HIP graph (launches, cross-stream joins and the
+dominant kernel's event records as graph nodes) and replayed, after one warm
+replay (the first launch of a graph uploads it); --eager issues them from the
+host launch by launch instead.  Inside the timed region events bracket every
+4th launch of the dominant kernel in each step (--time-stride; its first
+launch included): each bracketed launch puts two marker packets in the queue,
+about 7 us of step time on the mixed serving step.  Every event is created
+with hipEventDisableSystemFence, so recording one adds no cache write-back.
 
 Prints ONE JSON line: throughput in layer-tokens/s, the roofline of the
 dominant kernel (its per-launch HIP-event time inside the timed region, on
-the stream it runs on; the warm-up steps, timed per launch, pick it), every
-kernel's time from an instrumented pass after the timed region (the timed
-region brackets the dominant kernel only; every event is created with
-hipEventDisableSystemFence, so recording one adds no cache write-back), the
-CPU oracle timed on a
-bounded sample of the same workload over a pool of host processes, and a
+the stream it runs on; the warm-up steps, timed per launch, pick it by their
+median), every kernel's time from an instrumented pass after the timed
+region, the CPU oracle timed on a bounded sample of the same workload over a
+pool of host processes, and a
 cold-cache pass (`cold_cache`: up to 20 more steps, each after a 1 GiB read
 that evicts L2 and the Infinity Cache, timed with events; context beside
 `value`, which is the warm timed region).
@@ -323,6 +329,8 @@ class Plan:
 # ordered and visible through the kernels' own dispatch fences.
 HIP_EVENT_DISABLE_TIMING = 0x2
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+# hipStreamUpdateCaptureDependencies: replace the capture's dependency set
+HIP_STREAM_SET_CAPTURE_DEPENDENCIES = 0x1
 
 
 class HipEvents:
@@ -351,10 +359,32 @@ class HipEvents:
             raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
         return ev
 
-    def record(self, ev, stream):
-        rc = self.lib.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream))
+    def record(self, ev, stream, node=False):
+        """Record ev on stream.  node=True, for a stream under capture: add
+        an event-record node to the graph being captured, after the
+        stream's current dependencies, and make it the stream's only
+        dependency (an event recorded during capture is otherwise only an
+        ordering edge, and this runtime refuses hipEventRecordExternal)."""
+        ct, sp = self.ct, self.ct.c_void_p(stream.cuda_stream)
+        if not node:
+            rc = self.lib.hipEventRecord(ev, sp)
+            if rc != 0:
+                raise RuntimeError(f"hipEventRecord: {rc}")
+            return
+        status, cid, graph = ct.c_int(), ct.c_ulonglong(), ct.c_void_p()
+        deps, ndeps = ct.POINTER(ct.c_void_p)(), ct.c_size_t()
+        rc = self.lib.hipStreamGetCaptureInfo_v2(sp, ct.byref(status), ct.byref(cid), ct.byref(graph),
+                                                 ct.byref(deps), ct.byref(ndeps))
+        if rc != 0 or not graph:
+            raise RuntimeError(f"hipStreamGetCaptureInfo_v2: {rc} (is the stream capturing?)")
+        nd = ct.c_void_p()
+        rc = self.lib.hipGraphAddEventRecordNode(ct.byref(nd), graph, deps, ndeps, ev)
         if rc != 0:
-            raise RuntimeError(f"hipEventRecord: {rc}")
+            raise RuntimeError(f"hipGraphAddEventRecordNode: {rc}")
+        rc = self.lib.hipStreamUpdateCaptureDependencies(sp, ct.byref(nd), ct.c_size_t(1),
+                                                         ct.c_uint(HIP_STREAM_SET_CAPTURE_DEPENDENCIES))
+        if rc != 0:
+            raise RuntimeError(f"hipStreamUpdateCaptureDependencies: {rc}")
 
     def wait(self, stream, ev):
         rc = self.lib.hipStreamWaitEvent(self.ct.c_void_p(stream.cuda_stream), ev, self.ct.c_uint(0))
@@ -387,21 +417,32 @@ class Runner:
     def events(self):
         return [(self.hip.create(), self.hip.create()) for _ in range(self.n_runs)]
 
-    def step(self, ev=None, only=None):
+    def timed(self, only=None, stride=1):
+        """Indices (among the step's launches) that carry events: every
+        launch, or every stride-th launch of kernel `only`."""
+        names = [nm for nm, _ in self.plan.launches]
+        if only is None:
+            return set(range(len(names)))
+        return set([i for i, nm in enumerate(names) if nm == only][::stride])
+
+    def step(self, ev=None, only=None, capture=False, stride=1):
         """One step; with ev, launches are bracketed by their event pair
-        (only the launches of kernel `only` when it is given)."""
+        (every stride-th launch of kernel `only` when it is given).  capture:
+        the streams are being captured, and the timing records become
+        event-record nodes of the graph."""
         import torch
         i = 0
+        timed_set = self.timed(only, stride) if ev is not None else set()
         for op in self.plan.ops:
             if op[0] == "run":
                 st = self.streams[0 if self.serial else op[3]]
-                timed = ev is not None and (only is None or op[1] == only)
+                timed = i in timed_set
                 with torch.cuda.stream(st):
                     if timed:
-                        self.hip.record(ev[i][0], st)
+                        self.hip.record(ev[i][0], st, capture)
                     op[2]()
                     if timed:
-                        self.hip.record(ev[i][1], st)
+                        self.hip.record(ev[i][1], st, capture)
                 i += 1
             elif self.serial:
                 continue
@@ -410,28 +451,57 @@ class Runner:
             else:
                 self.hip.wait(self.streams[op[2]], self.marks[op[1]])
 
-    def stage_ms(self, ev, only=None):
-        """Per-kernel-name milliseconds of one step from its event pairs."""
-        out = {}
-        names = [nm for nm, _ in self.plan.launches]
-        for nm, (a, b) in zip(names, ev):
-            if only is None or nm == only:
-                out[nm] = out.get(nm, 0.0) + self.hip.elapsed(a, b)
-        return out
+    def capture(self, events=None, only=None, steps=1, stride=1):
+        """A HIP graph of `steps` steps (len(events) when events are given,
+        each step's timing records of kernel `only` captured as event-record
+        nodes).  The caller's stream hosts the capture and the side streams
+        join it through the plan's marks, so replaying the graph issues the
+        same launches with the same dependencies as step()."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        main = self.streams[0]
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.streams[0] = torch.cuda.current_stream()
+            try:
+                for i in range(len(events) if events is not None else steps):
+                    self.step(events[i] if events is not None else None, only=only, capture=True,
+                              stride=stride)
+            finally:
+                self.streams[0] = main
+        return g
 
-    def instrumented(self, steps):
-        """Per-kernel-name milliseconds per step, averaged over `steps`
-        steps with every launch bracketed by events."""
+    def stage_ms(self, ev, only=None, stride=1):
+        """Per-kernel-name milliseconds of one step from its event pairs (a
+        kernel timed on a stride-th of its launches: their mean times its
+        launch count)."""
+        acc, n = {}, {}
+        names = [nm for nm, _ in self.plan.launches]
+        timed_set = self.timed(only, stride)
+        for i, (nm, (a, b)) in enumerate(zip(names, ev)):
+            if i in timed_set:
+                acc[nm] = acc.get(nm, 0.0) + self.hip.elapsed(a, b)
+                n[nm] = n.get(nm, 0) + 1
+        return {nm: acc[nm] / n[nm] * self.plan.count[nm] for nm in acc}
+
+    def instrumented(self, steps, median=False):
+        """Per-kernel-name milliseconds per step over `steps` steps with
+        every launch bracketed by events: the mean, or with median=True the
+        median over the steps after the first (robust to a cold first step)."""
         import torch
         evs = [self.events() for _ in range(steps)]
         for ev in evs:
             self.step(ev)
         torch.cuda.synchronize()
-        acc = {}
-        for ev in evs:
-            for nm, ms in self.stage_ms(ev).items():
-                acc[nm] = acc.get(nm, 0.0) + ms / steps
-        return acc
+        per = [self.stage_ms(ev) for ev in evs]
+        if median and len(per) > 1:
+            per = per[1:]
+            out = {}
+            for nm in per[0]:
+                v = sorted(p[nm] for p in per)
+                out[nm] = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+            return out
+        return {nm: sum(p[nm] for p in per) / len(per) for nm in per[0]}
 
 
 def _layer_on_device(lb, dev):
@@ -557,17 +627,20 @@ def plan_long(dev, nseg=1):
     return p
 
 
-def plan_mixed(dev, fused=True):
-    """24 layers of the mixed serving step.  Per layer the decode tokens'
-    launch (fused conv + post-conv + step, or the step alone after a conv +
-    post-conv over all tokens when not fused) goes to side stream 1 once the
-    layer's conv + post-conv is done, and stream 0 waits for it before the
-    next layer: it runs beside the prefill, which touches other sequences."""
+def plan_mixed(dev, fused=True, layers=24, make_layer=None):
+    """`layers` layers of the mixed serving step (24; make_layer(layer)
+    gives a layer's inputs, inputs.mixed_serving_layer by default).  Per
+    layer the decode tokens' launch (fused conv + post-conv + step, or the
+    step alone after a conv + post-conv over all tokens when not fused) goes
+    to side stream 1 once the layer's conv + post-conv is done, and stream 0
+    waits for it before the next layer: it runs beside the prefill, which
+    touches other sequences."""
     from linear_attention_layers_amd import gdn, inputs
-    L = 24
+    L = layers
+    make_layer = make_layer or inputs.mixed_serving_layer
     p = Plan()
     for layer in range(L):
-        lb = inputs.mixed_serving_layer(layer)
+        lb = make_layer(layer)
         if layer == 0:
             p.lb = lb
         d = _layer_on_device(lb, dev)
@@ -737,6 +810,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true",
                     help="issue every launch on one stream (no side stream for the decode tokens)")
+    ap.add_argument("--time-stride", type=int, default=4,
+                    help="in the timed region, bracket every n-th launch of the dominant kernel in "
+                         "each step with events, its first launch included (1: every launch; each "
+                         "bracketed launch adds two marker packets to the queue)")
+    ap.add_argument("--eager", action="store_true",
+                    help="issue the timed steps' launches from the host one by one instead of "
+                         "replaying them as one captured HIP graph")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (steps run after a 1 GiB read that evicts L2 and the "
                          "256 MB Infinity Cache; reported beside the timed region, never as value)")
@@ -789,22 +869,36 @@ def main():
     stream = torch.cuda.current_stream()
     runner = Runner(plan, stream, serial=args.serial)
 
-    # warm-up steps with every launch timed: they pick the dominant kernel
+    # warm-up steps with every launch timed: the kernel with the largest
+    # median time per step over them (the first left out) is the dominant one
     names = list(dict.fromkeys(nm for nm, _ in plan.launches))
-    warm_ms = runner.instrumented(warmup)
+    warm_ms = runner.instrumented(warmup, median=True)
     dominant = max([nm for nm in names if plan.bytes.get(nm)], key=lambda nm: warm_ms[nm])
 
     # the timed region: K steps bracketed by synchronisation, events around
-    # the dominant kernel's launches only (on the stream each runs on)
+    # the dominant kernel's launches only (on the stream each runs on).  By
+    # default the K steps are captured once as a HIP graph (their launches,
+    # stream joins and the dominant kernel's event records as nodes) and the
+    # graph is replayed twice: a warm replay, then the timed one; --eager
+    # issues every launch from the host inside the timed region instead.
     events = [runner.events() for _ in range(steps)]
+    graph = None
+    if not args.eager:
+        graph = runner.capture(events, only=dominant, stride=args.time_stride)
+        graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        runner.step(events[i], only=dominant)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(steps):
+            runner.step(events[i], only=dominant, stride=args.time_stride)
     enqueued = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = sum(runner.stage_ms(ev, only=dominant)[dominant] for ev in events) / steps
+    dom_ms = sum(runner.stage_ms(ev, only=dominant, stride=args.time_stride)[dominant]
+                 for ev in events) / steps
+    del graph
 
     # every kernel's time from an instrumented pass after the timed region;
     # the dominant kernel's entry is the timed region's own measurement
@@ -854,6 +948,7 @@ def main():
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "host_enqueue_ms_per_step": round(enqueued * 1e3 / steps, 4),
+        "launch": "eager" if args.eager else "hip graph (the timed steps captured once, replayed)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

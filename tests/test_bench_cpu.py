@@ -89,3 +89,18 @@ def test_default_workload_is_the_mixed_serving_step():
     assert 'ap.add_argument("--workload", choices=sorted(PLANS), default="mixed")' in src
     lb, layers = bench.cpu_sample("mixed")
     assert layers == 24 and lb.geo.C == 6144 and lb.nseq == 32 and lb.N == sum(I.mixed_lengths())
+
+
+def test_timing_stride_picks_every_nth_launch_of_the_kernel():
+    p = bench.Plan()
+    for layer in range(6):
+        p.add("convpost", None, 1)
+        p.add("prefill", None, 1)
+        p.add("fused", None, 1, stream=1)
+    r = bench.Runner.__new__(bench.Runner)
+    r.plan = p
+    pre = [i for i, (nm, _) in enumerate(p.launches) if nm == "prefill"]
+    assert r.timed("prefill", 1) == set(pre)
+    assert r.timed("prefill", 4) == {pre[0], pre[4]}
+    assert r.timed("prefill", 24) == {pre[0]}
+    assert r.timed(None) == set(range(18))
