@@ -443,7 +443,7 @@ __global__ __launch_bounds__(64 * 64 / CPShape<T>::kTok) void conv_post_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) sv[i] = silu<T>(yv[i]);
     // every lane takes part in the row reduction (DPP needs its partners)
-    const float sum = head_sum_sq(sv);
+    const float sum = head_sum_sq<T>(sv);
     if (u < n) {
       if (is_qk) {
         const float inv = l2_inv<T>(sum, eps);

@@ -112,10 +112,16 @@ __device__ __forceinline__ bool seq_flag(const uint8_t* __restrict__ f, int s) {
 // ------------------------------------------------------- wave64 DPP moves
 // Row-local (16-lane) data movement.  quad_perm xor-1 = 0xB1, xor-2 = 0x4E,
 // row_half_mirror = 0x141 (lane i <- 7-i within 8), row_mirror = 0x140
-// (lane i <- 15-i within 16).
+// (lane i <- 15-i within 16); only controls whose every lane has a source
+// lane in its row (quad permutations and mirrors).  For those the bound_ctrl
+// bit changes no value, and with it set the compiler folds the move into the
+// arithmetic that consumes it (one v_add_f32_dpp instead of a DPP move, two
+// wait states and an add).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+  static_assert((CTRL >= 0x00 && CTRL <= 0xFF) || CTRL == 0x140 || CTRL == 0x141,
+                "dpp_mov is for quad permutations and row mirrors");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
 // Sum over the 16 lanes of a DPP row, result in every lane of the row.
@@ -165,7 +171,14 @@ template <> __device__ __forceinline__ float l2_inv<uint16_t>(float sum, float e
   return __builtin_amdgcn_rsqf(__builtin_fmaxf(sum + eps, 1.17549435e-38f));
 }
 
-__device__ __forceinline__ float head_sum_sq(const float (&s)[8]) {
+// Sum of squares of a head's 128 channels (8 per lane, 16 lanes).  A float32
+// output keeps the documented order: within the lane the pairwise tree
+// ((s0^2 + s1^2) + (s2^2 + s3^2)) + ((s4^2 + s5^2) + (s6^2 + s7^2)), each
+// square and sum rounded, then row16_sum.  A bf16 output only needs the sum
+// far inside a bf16 step, so the lane's part is two fused multiply-add
+// chains over channels 0-3 and 4-7, added (9 instead of 15 operations).
+template <class TO> __device__ __forceinline__ float head_sum_sq(const float (&s)[8]);
+template <> __device__ __forceinline__ float head_sum_sq<float>(const float (&s)[8]) {
 #pragma clang fp contract(off)
   const float p0 = s[0] * s[0] + s[1] * s[1];
   const float p1 = s[2] * s[2] + s[3] * s[3];
@@ -173,6 +186,15 @@ __device__ __forceinline__ float head_sum_sq(const float (&s)[8]) {
   const float p3 = s[6] * s[6] + s[7] * s[7];
   const float lane = (p0 + p1) + (p2 + p3);
   return row16_sum(lane);
+}
+template <> __device__ __forceinline__ float head_sum_sq<uint16_t>(const float (&s)[8]) {
+  float a = s[0] * s[0], b = s[4] * s[4];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    a = __builtin_fmaf(s[i], s[i], a);
+    b = __builtin_fmaf(s[4 + i], s[4 + i], b);
+  }
+  return row16_sum(a + b);
 }
 
 
@@ -183,7 +205,7 @@ __device__ __forceinline__ void postconv_lane(const float (&raw)[8], bool is_qk,
   float s[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = silu<TO>(raw[i]);
-  const float sum = head_sum_sq(s);
+  const float sum = head_sum_sq<TO>(s);
   const float inv = l2_inv<TO>(sum, eps);
 #pragma unroll
   for (int i = 0; i < 8; ++i) out[i] = is_qk ? s[i] * inv : s[i];

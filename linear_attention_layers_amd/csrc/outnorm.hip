@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void out_norm_kernel(const T* __restrict__ o, 
   const f32x4 w0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 32 * jl, 0, 0));
   const f32x4 w1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, 32 * jl + 16, 0, 0));
   // mean of squares over the head's 128 channels (1/128 is exact)
-  const float inv = 1.0f / __builtin_sqrtf(head_sum_sq(ov) * (1.0f / 128.0f) + eps);
+  const float inv = 1.0f / __builtin_sqrtf(head_sum_sq<float>(ov) * (1.0f / 128.0f) + eps);
   float yv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kPostThreads) void postconv_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) s[i] = silu<TO>(raw[u][i]);
     // every lane takes part in the row reduction (DPP needs its partners)
-    const float sum = head_sum_sq(s);
+    const float sum = head_sum_sq<TO>(s);
     if (!active || t >= N) continue;
     if (c0 < 2 * qk) {
       const float inv = l2_inv<TO>(sum, eps);
