@@ -203,6 +203,25 @@ template <> struct Act4<uint16_t> {
   }
 };
 
+// Work item of a conv launch (1-D grid): channel group `group` (the fastest
+// index) of chunk slot `slot`, the slots taken last to first, then the extra
+// slot `nslots` (empty sequences' rows) after every chunk.  Workgroups are
+// dispatched in index order, so the ones running at any moment cover whole
+// rows of x and of the outputs (every channel group of a few chunks:
+// contiguous memory spread over all HBM channels) rather than one channel
+// group of many chunks (pieces one row pitch apart, which crowd a few
+// channels: 87 against 75 us for the mixed serving layer's conv and
+// post-conv).  The first chunks of the sequences, which the prefill reads
+// first, are written last and are still in L2 when it starts.
+struct ConvItem {
+  int slot, group;
+};
+__device__ __forceinline__ ConvItem conv_item(int nslots, int ngroups) {
+  const int b = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+  const int r = b / ngroups;
+  return {r < nslots ? nslots - 1 - r : nslots, b - r * ngroups};
+}
+
 template <class T>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     const T* __restrict__ x, int64_t xs, const float* __restrict__ w, const float* __restrict__ bias,
@@ -210,12 +229,13 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(
     const gdn_chunk* __restrict__ chunks, int nslots, int nseq, int C, int write_state, T* __restrict__ y) {
   using A = Act4<T>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int c0 = (blockIdx.y * 64 + lane) * kConvChannelsPerLane;
-  if ((int)blockIdx.x == nslots) {   // launched only when write_state
+  const ConvItem it = conv_item(nslots, (C + kConvChannelsPerBlock - 1) / kConvChannelsPerBlock);
+  const int c0 = (it.group * 64 + lane) * kConvChannelsPerLane;
+  if (it.slot == nslots) {   // launched only when write_state
     if (wave == 0) zero_empty_conv_rows<kConvChannelsPerLane>(conv_state, has_init, cu, nseq, C, c0, lane);
     return;
   }
-  const gdn_chunk ch = chunks[blockIdx.x];
+  const gdn_chunk ch = chunks[it.slot];
   if (ch.seq < 0 || c0 >= C) return;
   const int s = ch.seq;
   const int t_begin = ch.begin + kConvTokensPerWave * wave;
@@ -360,12 +380,13 @@ __global__ __launch_bounds__(64 * 64 / CPShape<T>::kTok) void conv_post_kernel(
   constexpr int TPW = CPShape<T>::kTok;
   using AT = Act<T>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int c0 = (blockIdx.y * 64 + lane) * 8;
-  if ((int)blockIdx.x == nslots) {   // launched only when write_state
+  const ConvItem it = conv_item(nslots, (C + 511) / 512);
+  const int c0 = (it.group * 64 + lane) * 8;
+  if (it.slot == nslots) {   // launched only when write_state
     if (wave == 0) zero_empty_conv_rows<8>(conv_state, has_init, cu, nseq, C, c0, lane);
     return;
   }
-  const gdn_chunk ch = chunks != nullptr ? chunks[blockIdx.x] : derive_chunk(cu, nseq, blockIdx.x, lane);
+  const gdn_chunk ch = chunks != nullptr ? chunks[it.slot] : derive_chunk(cu, nseq, it.slot, lane);
   if (ch.seq < 0 || c0 >= C) return;   // whole 16-lane rows: C is a multiple of 128
   const int s = ch.seq;
   const int t_begin = ch.begin + TPW * wave;
@@ -500,10 +521,13 @@ hipError_t launch_conv_postconv(const void* x, int64_t xs, int act, const float*
                                 const gdn_chunk* chunks, int nchunks, int nseq, int Hk, int Hv, float eps,
                                 int write_state, void* q, void* k, void* v, hipStream_t st) {
   const int C = (2 * Hk + Hv) * 128;
-  // nchunks slots (descriptors, or the derived slots), and when the final
-  // rows are written one more column for the empty sequences
-  dim3 grid(nchunks + (write_state ? 1 : 0), (C + 511) / 512);
-  if (grid.x == 0) return hipSuccess;
+  // (nchunks slots, descriptors or derived, and when the final rows are
+  // written one more for the empty sequences) x channel groups, flattened
+  // (see conv_item)
+  const int64_t nblk = (int64_t)(nchunks + (write_state ? 1 : 0)) * ((C + 511) / 512);
+  if (nblk == 0) return hipSuccess;
+  if (nblk > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nblk);
   if (act == GDN_F32) {
     hipLaunchKernelGGL(conv_post_kernel<float>, grid, dim3(64 * 64 / CPShape<float>::kTok), 0, st,
                        static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks, nchunks, nseq,
@@ -522,10 +546,14 @@ hipError_t launch_conv(const void* x, int64_t xs, int act, const float* w, const
                        float* conv_state, const uint8_t* has_init, const int32_t* cu,
                        const gdn_chunk* chunks, int nchunks, int nseq, int C, int write_state, void* y,
                        hipStream_t st) {
-  // one column per chunk slot, and one for the empty sequences when the
-  // final rows are written
-  dim3 grid(nchunks + (write_state ? 1 : 0), (C + kConvChannelsPerBlock - 1) / kConvChannelsPerBlock);
-  if (grid.x == 0) return hipSuccess;
+  // one workgroup per chunk slot (and one more slot for the empty sequences
+  // when the final rows are written) and channel group, flattened (see
+  // conv_item)
+  const int64_t nblk = (int64_t)(nchunks + (write_state ? 1 : 0)) *
+                      ((C + kConvChannelsPerBlock - 1) / kConvChannelsPerBlock);
+  if (nblk == 0) return hipSuccess;
+  if (nblk > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nblk);
   if (act == GDN_F32) {
     hipLaunchKernelGGL(conv_kernel<float>, grid, dim3(kConvThreads), 0, st,
                        static_cast<const float*>(x), xs, w, bias, conv_state, has_init, cu, chunks,

@@ -32,10 +32,16 @@ template <class TI, class TO>
 __global__ __launch_bounds__(kPostThreads) void postconv_kernel(
     const TI* __restrict__ y, int64_t ys, int N, int C, int Hk, int Hv, float eps,
     TO* __restrict__ q, TO* __restrict__ k, TO* __restrict__ v) {
-  const int c0 = (blockIdx.y * kPostThreads + threadIdx.x) * 8;
+  // 1-D grid: channel group fastest, token blocks last to first, so the
+  // running workgroups cover whole rows (as the conv launches do)
+  const int ngroups = (C + kPostChannelsPerBlock - 1) / kPostChannelsPerBlock;
+  const int ntb = (N + kPostTokensPerBlock - 1) / kPostTokensPerBlock;
+  const int b = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+  const int r = b / ngroups;
+  const int c0 = ((b - r * ngroups) * kPostThreads + threadIdx.x) * 8;
   const bool active = c0 < C;
   const int qk = Hk * 128;
-  const int t0 = blockIdx.x * kPostTokensPerBlock;
+  const int t0 = (ntb - 1 - r) * kPostTokensPerBlock;
 
   float raw[kPostTokensPerBlock][8];
 #pragma unroll
@@ -73,8 +79,11 @@ template <class TI, class TO>
 hipError_t launch_t(const void* y, int64_t ys, int N, int Hk, int Hv, float eps, void* q, void* k,
                     void* v, hipStream_t st) {
   const int C = (2 * Hk + Hv) * 128;
-  dim3 grid((N + kPostTokensPerBlock - 1) / kPostTokensPerBlock,
-            (C + kPostChannelsPerBlock - 1) / kPostChannelsPerBlock);
+  const int64_t nblk = (int64_t)((N + kPostTokensPerBlock - 1) / kPostTokensPerBlock) *
+                      ((C + kPostChannelsPerBlock - 1) / kPostChannelsPerBlock);
+  if (nblk == 0) return hipSuccess;
+  if (nblk > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nblk);
   hipLaunchKernelGGL((postconv_kernel<TI, TO>), grid, dim3(kPostThreads), 0, st,
                      static_cast<const TI*>(y), ys, N, C, Hk, Hv, eps, static_cast<TO*>(q),
                      static_cast<TO*>(k), static_cast<TO*>(v));
