@@ -52,7 +52,7 @@ Other workloads (--workload), each one JSON line in the same form:
           the gated output norm on the mixed serving step's o, 24 layers
   gates   the gate computation for the mixed serving step, 24 layers
   long-seg
-          the 32768-token prefill split into 4 segments
+          the 32768-token prefill split into 5 segments
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
                   [--serial] [--workload mixed|varlen|verify|...]
@@ -750,7 +750,7 @@ def plan_gates(dev):
 PLANS = {"varlen": plan_varlen, "verify": plan_verify, "long": plan_long, "mixed": plan_mixed,
          "verify-fused": lambda dev: plan_verify(dev, fused=True),
          "mixed-unfused": lambda dev: plan_mixed(dev, fused=False), "out-norm": plan_out_norm,
-         "gates": plan_gates, "long-seg": lambda dev: plan_long(dev, nseg=4)}
+         "gates": plan_gates, "long-seg": lambda dev: plan_long(dev, nseg=5)}
 
 
 def cpu_sample(workload):

@@ -245,8 +245,11 @@ int gdn_delta_rule_prefill(const void* q, const void* k, const void* v, int act,
  * being affine in the state (the gated delta rule of item 4): a run of tokens
  * entering with S ends at S P + R, with P = M_1 ... M_n, M_t = a_t (I - b_t
  * k_t k_t^T) (dk x dk, independent of v) and R the end state from S = 0.
- * With n tokens and per = ceil(ceil(n / 64) / nseg), segment p covers tokens
- * [bos + min(n, 64 p per), bos + min(n, 64 (p + 1) per)).  Three launches:
+ * With n tokens in nc = ceil(n / 64) chunks, segment p covers chunks
+ * [b(p), b(p + 1)), b(0) = 0, b(nseg) = nc, b(p) = ceil(nc (2 p + 3) /
+ * (2 nseg + 3)): the first segment spans 5 of 2 nseg + 3 shares, every later
+ * one 2 (it is evaluated once, the later ones three times); tokens
+ * [bos + min(n, 64 b(p)), bos + min(n, 64 b(p + 1))).  Three launches:
  *   1. segment 0 from the entering state (its end state is X_1); each later
  *      segment p from S = 0 (R_p) and, with v = 0, from S = I (P_p);
  *   2. X_{p+1} = X_p P_p + R_p (float32), p = 1 .. nseg - 2;

@@ -472,9 +472,15 @@ __device__ __forceinline__ Prec<uint16_t>::F32 kq_fragT(const uint16_t* p, int c
   return f;
 }
 
-// Segment roles (SEG != 0).  A sequence is split into nseg segments of
-// whole chunks (segment p: tokens [bos + min(n, p per 64), bos + min(n,
-// (p + 1) per 64)), per = ceil(ceil(n / 64) / nseg)).  The per-token rule is
+// Segment roles (SEG != 0).  A sequence of nc = ceil(n / 64) chunks is split
+// into nseg segments of whole chunks: segment p covers chunks [b(p),
+// b(p + 1)), b(0) = 0, b(nseg) = nc, b(p) = ceil(nc (2 p + 3) / (2 nseg + 3)),
+// i.e. segment 0 spans 5 of 2 nseg + 3 shares and every later one 2 (tokens
+// clipped to n).  Segment 0 is evaluated once (first pass), a later one
+// three times (R, P, then the re-run), so a longer first segment shortens
+// the critical path: on one 32k-token sequence (32 v-heads) with 5
+// segments the two passes take about 15% less than with 4 equal ones.  The
+// per-token rule is
 // affine in the state, S_end = S_start P + R, so
 //   SEG = 1 (first pass): segment 0 runs from the entering state and writes
 //     its end state to X[1]; every later segment p runs twice over its
@@ -546,9 +552,13 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
   int bos = cu[s], eos = cu[s + 1];
   const bool init = seq_flag(has_init, s);   // requested with cu (both scalar)
   if (SEG != 0) {
-    const int n = eos - bos, per = ((n + BT - 1) / BT + nseg - 1) / nseg;
-    eos = bos + min(n, (p + 1) * per * BT);
-    bos = bos + min(n, p * per * BT);
+    const int n = eos - bos;
+    const int64_t nch = (n + BT - 1) / BT, shares = 2 * nseg + 3;
+    auto bound = [&](int pp) -> int {   // first chunk of segment pp
+      return pp == 0 ? 0 : pp >= nseg ? (int)nch : (int)((nch * (2 * pp + 3) + shares - 1) / shares);
+    };
+    eos = bos + min(n, bound(p + 1) * BT);
+    bos = bos + min(n, bound(p) * BT);
   }
   const int nc = eos > bos ? (eos - bos + BT - 1) / BT : 0;
   // valid tokens of chunk c (0 past the end)

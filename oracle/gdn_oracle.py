@@ -335,19 +335,24 @@ def delta_rule_chunked(q, k, v, g, beta, state0, has_init, cu_seqlens, Hk, Hv,
 def segment_bounds(cu_seqlens, nseg: int, chunk_len: int = 64) -> np.ndarray:
     """Split of every sequence into nseg segments of whole chunks, for the
     segment-parallel evaluation below.  The pages print no such split
-    (reading): with n tokens, nc = ceil(n / chunk_len) chunks and per =
-    ceil(nc / nseg) chunks per segment, segment p covers tokens
-    [bos + min(n, p per chunk_len), bos + min(n, (p + 1) per chunk_len)), so
-    the last segments may be short or empty.  Returns int64 [nseq, nseg, 2]
-    (begin, end)."""
+    (reading; any split gives the same result, the split only decides which
+    transitions exist): with n tokens and nc = ceil(n / chunk_len) chunks,
+    segment p covers chunks [b(p), b(p + 1)) with b(0) = 0, b(nseg) = nc and
+        b(p) = ceil(nc (2 p + 3) / (2 nseg + 3)),   0 < p < nseg,
+    i.e. the first segment spans 5 of the 2 nseg + 3 shares and every later
+    one 2, and tokens [bos + min(n, b(p) chunk_len), bos + min(n, b(p + 1)
+    chunk_len)); the last segments may be short or empty.  Returns int64
+    [nseq, nseg, 2] (begin, end)."""
     cu = [int(c) for c in cu_seqlens]
     out = np.zeros((len(cu) - 1, nseg, 2), dtype=np.int64)
+    shares = 2 * nseg + 3
     for s in range(len(cu) - 1):
         n = cu[s + 1] - cu[s]
-        per = -(-(-(-n // chunk_len)) // nseg)
+        nc = -(-n // chunk_len)
+        b = [0] + [-(-(nc * (2 * p + 3)) // shares) for p in range(1, nseg)] + [nc]
         for p in range(nseg):
-            out[s, p, 0] = cu[s] + min(n, p * per * chunk_len)
-            out[s, p, 1] = cu[s] + min(n, (p + 1) * per * chunk_len)
+            out[s, p, 0] = cu[s] + min(n, b[p] * chunk_len)
+            out[s, p, 1] = cu[s] + min(n, b[p + 1] * chunk_len)
     return out
 
 

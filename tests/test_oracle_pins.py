@@ -862,9 +862,14 @@ def test_transition_pins_catch_planted_mutation(kind):
 
 
 def test_segment_bounds_split_whole_chunks():
-    # 300 tokens, chunks of 64 -> 5 chunks, 2 per segment: [0,128) [128,256) [256,300)
+    # 300 tokens, chunks of 64 -> 5 chunks in 9 shares (5 for the first
+    # segment, 2 for each later one): chunk bounds 0, ceil(25/9) = 3,
+    # ceil(35/9) = 4, 5 -> [0,192) [192,256) [256,300)
     b = O.segment_bounds([0, 300], 3)
-    assert b[0].tolist() == [[0, 128], [128, 256], [256, 300]]
+    assert b[0].tolist() == [[0, 192], [192, 256], [256, 300]]
+    # 512 chunks in 5 segments (13 shares): 197 | 79 | 79 | 79 | 78 chunks
+    b = O.segment_bounds([0, 512 * 64], 5)
+    assert ((b[0, :, 1] - b[0, :, 0]) // 64).tolist() == [197, 79, 79, 79, 78]
     # more segments than chunks: trailing segments are empty, at the end
     b = O.segment_bounds([10, 75], 4)
     assert b[0].tolist() == [[10, 74], [74, 75], [75, 75], [75, 75]]
