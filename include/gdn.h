@@ -34,7 +34,11 @@
  *     segmented prefill takes a caller-owned workspace), keeps no state
  *     between calls and is safe to call from several host threads.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *     stream).  A returned GDN_OK means the launch was accepted.
+ *     stream).  A returned GDN_OK means the launch was accepted.  A call
+ *     only launches kernels on that stream (no allocation, copy, memset or
+ *     synchronisation), so it can be recorded by HIP stream capture and
+ *     replayed from a graph; the replay reads the buffers' contents at
+ *     replay time.
  *   - Activations are float32 (GDN_F32) or bfloat16 (GDN_BF16); conv weights,
  *     gates and both states are float32.  Head sizes dk = dv = 128.
  *   - Packed channels: C = 2*Hk*dk + Hv*dv, laid out q | k | v.  v-head h
