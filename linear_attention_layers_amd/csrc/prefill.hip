@@ -1151,47 +1151,77 @@ hipError_t launch_ws(const void* q, const void* k, const void* v, const float* g
 // The segment chain X[p + 1] = X[p] P[p] + R[p], p = 1 .. nseg - 2, for one
 // 16-row block of one (sequence, v-head).  Rows of the chain are
 // independent (row i of X[p + 1] needs row i of X[p] and all of P[p]), so
-// every block runs its own chain.  Thread (r, cg) forms row 16 rb + r,
-// columns 8 cg .. 8 cg + 7, in float32 with the products added in k order.
+// every block runs its own chain, in float32 on 16x16x4 MFMAs: wave w forms
+// columns 32 w .. 32 w + 31 (two 16x16 tiles) from the block's X rows and
+// P, both staged in LDS, starting from R.  Rows of the LDS copies are padded
+// to 132 floats, so a fragment's four strided P rows and its sixteen X rows
+// each fall on distinct banks.
 __global__ __launch_bounds__(256) void seg_combine_kernel(float* ws, int nseq, int nseg, int Hv) {
-  __shared__ float Pl[DK * DK];
-  __shared__ float Xl[16 * DK];
-  const int rb = blockIdx.x & 7, h = (blockIdx.x >> 3) % Hv, s = (blockIdx.x >> 3) / Hv;
-  const int tid = threadIdx.x, r = tid >> 4, cg = tid & 15;
-  const int row = 16 * rb + r;
+  constexpr int LD = DK + 4;
+  __shared__ float Pl[DK * LD];
+  __shared__ float Xl[16 * LD];
+  // block b runs on XCD b % 8 (round-robin dispatch); when the units
+  // (sequence, v-head) come in eights, the 8 row blocks of a unit share b % 8,
+  // so the unit's P is fetched into one XCD's L2
+  const int blk = blockIdx.x;
+  const bool by_xcd = ((nseq * Hv) & 7) == 0;
+  const int unit = by_xcd ? (blk & 7) + 8 * (blk >> 6) : blk >> 3;
+  const int rb = by_xcd ? (blk >> 3) & 7 : blk & 7;
+  const int h = unit % Hv, s = unit / Hv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
   auto wsp = [&](int which, int pp) {
     return ws + ((((int64_t)which * nseq + s) * nseg + pp) * Hv + h) * (DK * DK);
   };
-  auto load8 = [](const float* p, float (&x)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  };
-  float x[8];
-  load8(wsp(0, 1) + row * DK + 8 * cg, x);
-  for (int p = 1; p + 1 < nseg; ++p) {
-    __syncthreads();   // the previous step is done with Pl and Xl
-    const float4* Pp = reinterpret_cast<const float4*>(wsp(2, p));
-#pragma unroll 4
-    for (int i = tid; i < DK * DK / 4; i += 256) reinterpret_cast<float4*>(Pl)[i] = Pp[i];
-    *reinterpret_cast<float4*>(&Xl[r * DK + 8 * cg]) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(&Xl[r * DK + 8 * cg + 4]) = make_float4(x[4], x[5], x[6], x[7]);
-    __syncthreads();
-    float acc[8];
-    load8(wsp(1, p) + row * DK + 8 * cg, acc);
-    for (int kk = 0; kk < DK; ++kk) {
-      const float xv = Xl[r * DK + kk];
-      const float4 p0 = *reinterpret_cast<const float4*>(&Pl[kk * DK + 8 * cg]);
-      const float4 p1 = *reinterpret_cast<const float4*>(&Pl[kk * DK + 8 * cg + 4]);
-      acc[0] = __builtin_fmaf(xv, p0.x, acc[0]); acc[1] = __builtin_fmaf(xv, p0.y, acc[1]);
-      acc[2] = __builtin_fmaf(xv, p0.z, acc[2]); acc[3] = __builtin_fmaf(xv, p0.w, acc[3]);
-      acc[4] = __builtin_fmaf(xv, p1.x, acc[4]); acc[5] = __builtin_fmaf(xv, p1.y, acc[5]);
-      acc[6] = __builtin_fmaf(xv, p1.z, acc[6]); acc[7] = __builtin_fmaf(xv, p1.w, acc[7]);
-    }
-    float* Xn = wsp(0, p + 1) + row * DK + 8 * cg;
-    *reinterpret_cast<float4*>(Xn) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4*>(Xn + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  // a 128-column matrix of ROWS rows from global memory into LDS rows of LD
+  // floats: every piece of a thread is requested before the first is
+  // written, so the copy waits for one memory latency, not one per piece
+  auto stage = [&](float* dst, const float* src, auto rows_c) {
+    constexpr int N = decltype(rows_c)::value * (DK / 4) / 256;
+    f32x4 t[N];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = acc[i];
+    for (int j = 0; j < N; ++j) t[j] = reinterpret_cast<const f32x4*>(src)[tid + 256 * j];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = tid + 256 * j;
+      *reinterpret_cast<f32x4*>(&dst[(i >> 5) * LD + 4 * (i & 31)]) = t[j];
+    }
+  };
+  stage(Xl, wsp(0, 1) + 16 * rb * DK, std::integral_constant<int, 16>{});
+  for (int p = 1; p + 1 < nseg; ++p) {
+    stage(Pl, wsp(2, p), std::integral_constant<int, DK>{});
+    __syncthreads();   // P[p] and X[p] are in LDS
+    const float* Rp = wsp(1, p) + 16 * rb * DK;
+    f32x4 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[j][e] = Rp[(4 * kg + e) * DK + 32 * w + 16 * j + r16];
+#pragma unroll 4
+    for (int kb = 0; kb < DK; kb += 16) {
+      // lane (r16, kg), slot t: X[r16][kb + 4 kg + t] and P[kb + 4 kg + t][column]
+      const float4 xa = *reinterpret_cast<const float4*>(&Xl[r16 * LD + kb + 4 * kg]);
+      const f32x4 a = f32x4{xa.x, xa.y, xa.z, xa.w};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = 32 * w + 16 * j + r16;
+        f32x4 b;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = Pl[(kb + 4 * kg + t) * LD + c];
+        acc[j] = Prec<float>::mma4x(a, b, acc[j]);
+      }
+    }
+    __syncthreads();   // every wave is done with Xl and Pl
+    // lane (r16, kg) holds rows 4 kg + e of columns 32 w + 16 j + r16
+    float* Xn = wsp(0, p + 1) + 16 * rb * DK;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 32 * w + 16 * j + r16;
+        Xn[(4 * kg + e) * DK + c] = acc[j][e];
+        Xl[(4 * kg + e) * LD + c] = acc[j][e];
+      }
   }
 }
 
