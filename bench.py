@@ -883,9 +883,18 @@ def main():
     # issues every launch from the host inside the timed region instead.
     events = [runner.events() for _ in range(steps)]
     graph = None
+    launch = "eager"
     if not args.eager:
-        graph = runner.capture(events, only=dominant, stride=args.time_stride)
-        graph.replay()
+        try:
+            graph = runner.capture(events, only=dominant, stride=args.time_stride)
+            graph.replay()
+            launch = "hip graph (the timed steps captured once, replayed)"
+        except (RuntimeError, torch.cuda.CudaError) as exc:
+            # a runtime that cannot capture these launches still gets its
+            # measurement, issued launch by launch (and says so)
+            graph = None
+            torch.cuda.synchronize()
+            launch = f"eager (graph capture failed: {str(exc).splitlines()[0][:120]})"
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graph is not None:
@@ -948,7 +957,7 @@ def main():
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "host_enqueue_ms_per_step": round(enqueued * 1e3 / steps, 4),
-        "launch": "eager" if args.eager else "hip graph (the timed steps captured once, replayed)",
+        "launch": launch,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
