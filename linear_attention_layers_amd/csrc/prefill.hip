@@ -426,7 +426,9 @@ constexpr int kOrderMax = 64;            // batches up to this size run longest 
 // 2 ((r / 8) % 2).  A fragment read (32 lanes: 16 rows x 2 granules) and a
 // transposing read (32 lanes: 8 rows x 4 consecutive granules) then both
 // touch each of the 64 LDS banks exactly once; no plain row padding does
-// that for both patterns.  Each 16-row block is followed by 16 bytes of
+// that for both patterns.  sig(r) is even, so granules 2m and 2m + 1 stay
+// adjacent: a 16-byte read of them (16 lanes: 16 rows) also covers the 64
+// banks once.  Each 16-row block is followed by 16 bytes of
 // padding, which shifts a block's banks uniformly (a read never spans two
 // blocks) but keeps any two blocks, and the same position in a K and a Q
 // tile, from lying a multiple of 512 bytes apart: the compiler would fuse
@@ -457,6 +459,17 @@ __device__ __forceinline__ Prec<uint16_t>::F32 kq_frag(const uint16_t* p, int ro
   const uint2 b = *reinterpret_cast<const uint2*>(p + kq_at(row, (kb >> 2) + 4 + kg));
   Prec<uint16_t>::F32 f;
   f.v = make_uint4(a.x, a.y, b.x, b.y);
+  return f;
+}
+
+// Fragment of a swizzled K / Q tile with the natural contraction order: lane
+// (r16, kg) holds k = 32 t + 8 kg .. + 7, logical granules 8 t + 2 kg and
+// + 1, which the (even) swizzle keeps adjacent and 16-byte aligned: one
+// 16-byte read.  Only for products whose two operands both come from K / Q
+// tiles (the tile pairs).
+__device__ __forceinline__ Prec<uint16_t>::F32 kq_frag_nat(const uint16_t* p, int row, int t, int kg) {
+  Prec<uint16_t>::F32 f;
+  f.v = *reinterpret_cast<const uint4*>(p + kq_at(row, 8 * t + 2 * kg));
   return f;
 }
 
@@ -659,23 +672,23 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       f32x4 kk0 = zero4(), qk0 = zero4(), kk1 = zero4(), qk1 = zero4(), kk2 = zero4(), qk2 = zero4();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const auto d0 = kq_frag(Kb, 16 * bd + r16, 32 * t, kg);
-        const auto b1 = kq_frag(Kb, 16 * bj1 + r16, 32 * t, kg);
-        const auto a1 = kq_frag(Kb, 16 * bi1 + r16, 32 * t, kg);
+        const auto d0 = kq_frag_nat(Kb, 16 * bd + r16, t, kg);
+        const auto b1 = kq_frag_nat(Kb, 16 * bj1 + r16, t, kg);
+        const auto a1 = kq_frag_nat(Kb, 16 * bi1 + r16, t, kg);
         kk0 = PR::mma32(d0, d0, kk0);
         kk1 = PR::mma32(b1, a1, kk1);
         if constexpr (WO) {
-          const auto q0 = kq_frag(Qb, 16 * bd + r16, 32 * t, kg);
-          const auto q1 = kq_frag(Qb, 16 * bi1 + r16, 32 * t, kg);
+          const auto q0 = kq_frag_nat(Qb, 16 * bd + r16, t, kg);
+          const auto q1 = kq_frag_nat(Qb, 16 * bi1 + r16, t, kg);
           qk0 = PR::mma32(d0, q0, qk0);
           qk1 = PR::mma32(b1, q1, qk1);
         }
         if constexpr (kThird) {
-          const auto b2 = kq_frag(Kb, 16 * bj2 + r16, 32 * t, kg);
-          const auto a2 = kq_frag(Kb, 16 * bi2 + r16, 32 * t, kg);
+          const auto b2 = kq_frag_nat(Kb, 16 * bj2 + r16, t, kg);
+          const auto a2 = kq_frag_nat(Kb, 16 * bi2 + r16, t, kg);
           kk2 = PR::mma32(b2, a2, kk2);
           if constexpr (WO) {
-            const auto q2 = kq_frag(Qb, 16 * bi2 + r16, 32 * t, kg);
+            const auto q2 = kq_frag_nat(Qb, 16 * bi2 + r16, t, kg);
             qk2 = PR::mma32(b2, q2, qk2);
           }
         }
