@@ -145,11 +145,11 @@ __global__ __launch_bounds__(256) void make_chunks_kernel(const int32_t* __restr
 // ------------------------------------------------- empty sequences
 // A sequence with no tokens has no chunk, so no chunk workgroup owns its
 // conv_state.  Its final rows are its initial rows: unchanged with an
-// initial state, zeros without one.  One extra workgroup column (launched
-// only when the final rows are written) takes the second case: wave 0
-// finds the empty sequences without an initial state 64 at a time (lane =
-// sequence, one ballot) and its lanes store zeros into the three rows of
-// their CPL channels of the column's channel group.
+// initial state, zeros without one.  One extra slot (a workgroup per
+// channel group, launched only when the final rows are written) takes the
+// second case: wave 0 finds the empty sequences without an initial state
+// 64 at a time (lane = sequence, one ballot) and its lanes store zeros into
+// the three rows of their CPL channels of the workgroup's channel group.
 template <int CPL>
 __device__ __forceinline__ void zero_empty_conv_rows(float* conv_state, const uint8_t* __restrict__ has_init,
                                                      const int32_t* __restrict__ cu, int nseq, int C, int c0,
@@ -179,7 +179,7 @@ __device__ __forceinline__ void zero_empty_conv_rows(float* conv_state, const ui
 // group.  A lane issues its 3 halo rows and its 16 token rows up front (19
 // independent loads), then computes and stores 16 outputs.  Only wave 0 of
 // a sequence's first chunk touches conv_state (see the file comment); the
-// column past the last slot clears the rows of empty sequences.
+// slot past the last chunk slot clears the rows of empty sequences.
 // Four adjacent activations in storage form.
 template <class T> struct Act4;
 template <> struct Act4<float> {
