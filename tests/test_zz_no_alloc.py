@@ -2,8 +2,9 @@
 scratch inside the library) against the allocating entry point with a
 caller workspace: same kernels, so the outputs and final states must be
 bitwise equal.  Two calls in a row, the second on a smaller input (the
-scratch keeps the first call's contents), then a call over the scratch
-limit, which must be refused before any launch."""
+scratch keeps the first call's contents); the call recorded into a HIP graph
+by stream capture and replayed; then a call over the scratch limit, which
+must be refused before any launch."""
 import pytest
 import torch
 
@@ -45,6 +46,32 @@ def test_noalloc_equals_workspace_entry_point_on_two_calls():
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"call {i}: o differs"
         assert torch.equal(st1.view(torch.int32), st2.view(torch.int32)), f"call {i}: state differs"
         assert torch.isfinite(o1.float()).all() and torch.isfinite(st1).all()
+
+
+def test_noalloc_replays_from_a_captured_graph():
+    # the callers this entry point is for: launches recorded by stream
+    # capture and replayed; each replay (after eager restores of the state
+    # and poisoned outputs) must give the eager call's bits
+    geo, lengths, hinit, nseg = CASES[0]
+    lb = I.make_layer(geo, lengths, "bf16", 1960, state_std=0.3, has_init=hinit)
+    out = TL.gpu_layer(lb)
+    args = (out["q"], out["k"], out["v"], out["g"], out["beta"], out["cu"])
+    st0 = lb.state.to(DEV).contiguous()
+    st, o = st0.clone(), torch.empty_like(out["v"])
+    gdn.gdn_delta_rule_prefill_segmented_noalloc(*args, st, nseg, out["hi"], o=o)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stc, oc = st0.clone(), torch.empty_like(o)
+    with torch.cuda.graph(graph):
+        gdn.gdn_delta_rule_prefill_segmented_noalloc(*args, stc, nseg, out["hi"], o=oc)
+    for rep in range(3):
+        stc.copy_(st0)
+        oc.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oc.view(torch.int16), o.view(torch.int16)), f"replay {rep}: o differs"
+        assert torch.equal(stc.view(torch.int32), st.view(torch.int32)), f"replay {rep}: state differs"
 
 
 def test_noalloc_refuses_more_than_its_scratch():
