@@ -585,8 +585,11 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
   if (wave >= 4) {
     // ================================================================ producers
     if (nc == 0) return;
-    auto produce = [&](auto wo_c) __attribute__((always_inline)) {
+    auto produce = [&](auto wo_c, auto rw_c) __attribute__((always_inline)) {
     constexpr bool WO = decltype(wo_c)::value;
+    // the wave's index within its role as a compile-time constant: its tile
+    // pairs' block offsets fold into the LDS instructions
+    constexpr int rw = decltype(rw_c)::value;
     const int ptid = tid - 256;
     u32x4 pk[KQ_ITEMS], pq[KQ_ITEMS];
     float gr = 0.f, br = 0.f;
@@ -635,7 +638,9 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     // P and -A of tile pair (bi, bj), bi >= bj, from its products kk, qk:
     // lane (r16, kg) holds rows i = 16 bi + r16, columns j = 16 bj + 4 kg + e
     // (transposed products: K_bj-rows as the A operand)
-    auto pair_store = [&](bool diag, int bi, int bj, f32x4 kk, f32x4 qk, int kb, int ab) __attribute__((always_inline)) {
+    auto pair_store = [&](auto diag_c, int bi, int bj, f32x4 kk, f32x4 qk, int kb, int ab) __attribute__((always_inline)) {
+      // off the diagonal every column precedes every row: no masks
+      constexpr bool diag = decltype(diag_c)::value;
       const float* Wl = &sm.W[kb][0][0];
       const int i = 16 * bi + r16, j0 = 16 * bj + 4 * kg;
       const float Li = Wl[i], bti = Wl[2 * BT + i];
@@ -644,13 +649,19 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       float pv[4], av[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float dec = j0 + e <= i ? __builtin_amdgcn_exp2f(Li - lj[e]) : 0.f;
-        pv[e] = dec * qk[e];
-        av[e] = j0 + e < i ? bti * dec * kk[e] : 0.f;
+        if constexpr (diag) {
+          const float dec = j0 + e <= i ? __builtin_amdgcn_exp2f(Li - lj[e]) : 0.f;
+          pv[e] = dec * qk[e];
+          av[e] = j0 + e < i ? bti * dec * kk[e] : 0.f;
+        } else {
+          const float dec = __builtin_amdgcn_exp2f(Li - lj[e]);
+          pv[e] = dec * qk[e];
+          av[e] = bti * dec * kk[e];
+        }
       }
       if constexpr (WO)
         *reinterpret_cast<u32x2*>(&sm.P[ab][i * LDT + j0]) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-      if (diag)
+      if constexpr (diag)
         *reinterpret_cast<float4*>(&sm.Ad[rw][r16][4 * kg]) = make_float4(av[0], av[1], av[2], av[3]);
       else
         *reinterpret_cast<u32x2*>(&sm.AT[ab][i * LDT + j0]) =
@@ -667,8 +678,8 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       const uint16_t* Kb = sm.K[kb];
       const uint16_t* Qb = sm.Q[kb];
       const int bd = rw;                                   // diagonal block
-      const int bi1 = rw < 3 ? rw + 1 : 2, bj1 = rw < 3 ? rw : 0;
-      const int bi2 = 3, bj2 = rw == 0 ? 1 : 0;
+      constexpr int bi1 = rw < 3 ? rw + 1 : 2, bj1 = rw < 3 ? rw : 0;
+      constexpr int bi2 = 3, bj2 = rw == 0 ? 1 : 0;
       f32x4 kk0 = zero4(), qk0 = zero4(), kk1 = zero4(), qk1 = zero4(), kk2 = zero4(), qk2 = zero4();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -693,13 +704,12 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           }
         }
       }
-      pair_store(true, bd, bd, kk0, qk0, kb, ab);
-      pair_store(false, bi1, bj1, kk1, qk1, kb, ab);
-      if constexpr (kThird) pair_store(false, bi2, bj2, kk2, qk2, kb, ab);
+      pair_store(std::true_type{}, bd, bd, kk0, qk0, kb, ab);
+      pair_store(std::false_type{}, bi1, bj1, kk1, qk1, kb, ab);
+      if constexpr (kThird) pair_store(std::false_type{}, bi2, bj2, kk2, qk2, kb, ab);
     };
     auto pairs = [&](int kb, int ab) __attribute__((always_inline)) {
-      if (rw < 2) pairs_t(std::true_type{}, kb, ab);
-      else pairs_t(std::false_type{}, kb, ab);
+      pairs_t(std::integral_constant<bool, (rw < 2)>{}, kb, ab);
     };
     // T_bb = (I + A_bb)^-1 of this wave's diagonal block b = rw, by forward
     // substitution.  Lane (c, q) = (lane / 4, lane % 4) owns rows q, q+4,
@@ -708,11 +718,15 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     // j >= i vanish: A_bb is strictly lower triangular.
     auto invert_diag = [&](int ab) {
       const int c = lane >> 2, qd = lane & 3, bb = rw;
+      // row q + 4 m has nonzero entries only in columns j < q + 4 m <= 4 m + 3,
+      // so its columns past 4 m + 2 are neither read nor applied (they are
+      // zero, and subtracting a zero product leaves x unchanged), and x_15
+      // feeds no row
       float arow[4][16];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
+        for (int j4 = 0; j4 <= m; ++j4) {
           const float4 t = *reinterpret_cast<const float4*>(&sm.Ad[rw][qd + 4 * m][4 * j4]);
           arow[m][4 * j4] = t.x; arow[m][4 * j4 + 1] = t.y;
           arow[m][4 * j4 + 2] = t.z; arow[m][4 * j4 + 3] = t.w;
@@ -721,10 +735,11 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
 #pragma unroll
       for (int m = 0; m < 4; ++m) x[m] = (qd + 4 * m == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < 15; ++j) {
         const float xj = quad_bcast(x[j >> 2], j & 3);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) x[m] = __builtin_fmaf(-arow[m][j], xj, x[m]);
+        for (int m = 0; m < 4; ++m)
+          if (j <= 4 * m + 2) x[m] = __builtin_fmaf(-arow[m][j], xj, x[m]);
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + 16 * bb + c], x[m]);
@@ -737,22 +752,22 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     };
 
     load_kq(0);
-    if (rw == 3) load_gates(0);
+    if constexpr (rw == 3) load_gates(0);
     stage_kq(0);
-    if (rw == 3) scan(0);
+    if constexpr (rw == 3) scan(0);
     load_kq(1);
-    if (rw == 3) load_gates(1);
+    if constexpr (rw == 3) load_gates(1);
     __syncthreads();
     factors(0);
     stage_kq(1);
-    if (rw == 3) scan(1);
+    if constexpr (rw == 3) scan(1);
     load_kq(2);
-    if (rw == 3) load_gates(2);
+    if constexpr (rw == 3) load_gates(2);
     __syncthreads();
     for (int c = 0; c < nc; ++c) {
       stage_kq((c + 2) % 3);
       load_kq(c + 3);
-      if (rw == 3) {
+      if constexpr (rw == 3) {
         scan(c + 2);
         load_gates(c + 3);
       }
@@ -760,11 +775,19 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       __syncthreads();
     }
     };
+    auto by_wave = [&](auto wo_c) __attribute__((always_inline)) {
+      switch (rw) {
+        case 0: produce(wo_c, std::integral_constant<int, 0>{}); break;
+        case 1: produce(wo_c, std::integral_constant<int, 1>{}); break;
+        case 2: produce(wo_c, std::integral_constant<int, 2>{}); break;
+        default: produce(wo_c, std::integral_constant<int, 3>{}); break;
+      }
+    };
     if constexpr (SEG == 1) {
-      if (o_on_wg) produce(std::true_type{});
-      else produce(std::false_type{});
+      if (o_on_wg) by_wave(std::true_type{});
+      else by_wave(std::false_type{});
     } else {
-      produce(std::true_type{});
+      by_wave(std::true_type{});
     }
     return;
   }
