@@ -913,14 +913,17 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     __syncthreads();
     __syncthreads();
 
-    // The loop runs two chunks per trip so that the factor buffer (ab =
-    // c & 1) and the V / o tile of each chunk are compile-time constants:
-    // their LDS offsets fold into the read instructions (32k prefill -2%).
-    auto iteration = [&](int c, auto ab_c) __attribute__((always_inline)) {
-      constexpr int ab = decltype(ab_c)::value;   // c & 1
+    // The loop runs three chunks per trip so that the K / Q and gate buffer
+    // of each chunk (kb = c % 3) is a compile-time constant: the offsets of
+    // its 96 fragment reads fold into the instructions, leaving the factor
+    // and V / o tiles' (ab = c & 1) few reads with a computed base (mixed
+    // serving layer -1%, varlen batch -2% against two chunks per trip with
+    // ab constant; six per trip, both constant, spills).
+    auto iteration = [&](int c, auto kb_c) __attribute__((always_inline)) {
+      constexpr int kb = decltype(kb_c)::value;   // c % 3
+      const int ab = c & 1;
       const int n = chunk_len(c);
       const int64_t c0 = bos + BT * c;
-      const int kb = c % 3;
       const uint16_t* Kc = sm.K[kb];
       const uint16_t* Qc = sm.Q[kb];
       const uint16_t* ATc = sm.AT[ab];
@@ -1152,9 +1155,12 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       }
       __syncthreads();
     };
-    for (int c = 0; c < nc; c += 2) {
+    for (int c = 0; c < nc; c += 3) {
       iteration(c, std::integral_constant<int, 0>{});
-      if (c + 1 < nc) iteration(c + 1, std::integral_constant<int, 1>{});
+      if (c + 1 >= nc) break;
+      iteration(c + 1, std::integral_constant<int, 1>{});
+      if (c + 2 >= nc) break;
+      iteration(c + 2, std::integral_constant<int, 2>{});
     }
     if (WO) {
       read_o((nc - 1) & 1);
