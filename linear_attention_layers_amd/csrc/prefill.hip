@@ -625,11 +625,11 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     };
     // cumulative log2-decay of chunk c and the vectors derived from it;
     // lanes past the chunk's end hold g = beta = 0
-    auto scan = [&](int c) {
+    auto scan = [&](int c, int buf) {
       const int n = chunk_len(c);
       const float L = wave_prefix_sum(gr) * kLog2e;
       const float Llast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(L), max(n, 1) - 1));
-      float* Wc = &sm.W[c % 3][0][0];
+      float* Wc = &sm.W[buf][0][0];
       Wc[lane] = L;
       Wc[BT + lane] = __builtin_amdgcn_exp2f(L);
       Wc[2 * BT + lane] = br;
@@ -745,34 +745,45 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + 16 * bb + c], x[m]);
     };
     // all factors of chunk c (K/Q and gate buffer c % 3 -> factor buffer c & 1)
-    auto factors = [&](int c) __attribute__((always_inline)) {
+    auto factors = [&](int c, int kb) __attribute__((always_inline)) {
       const int ab = c & 1;
-      pairs(c % 3, ab);
+      pairs(kb, ab);
       invert_diag(ab);
     };
 
     load_kq(0);
     if constexpr (rw == 3) load_gates(0);
     stage_kq(0);
-    if constexpr (rw == 3) scan(0);
+    if constexpr (rw == 3) scan(0, 0);
     load_kq(1);
     if constexpr (rw == 3) load_gates(1);
     __syncthreads();
-    factors(0);
+    factors(0, 0);
     stage_kq(1);
-    if constexpr (rw == 3) scan(1);
+    if constexpr (rw == 3) scan(1, 1);
     load_kq(2);
     if constexpr (rw == 3) load_gates(2);
     __syncthreads();
-    for (int c = 0; c < nc; ++c) {
-      stage_kq((c + 2) % 3);
+    // three chunks per trip: the K / Q buffers staged and read are
+    // compile-time constants, so the fragment offsets fold into the
+    // LDS instructions
+    auto step = [&](int c, auto m_c) __attribute__((always_inline)) {
+      constexpr int m = decltype(m_c)::value;   // c % 3
+      stage_kq((m + 2) % 3);
       load_kq(c + 3);
       if constexpr (rw == 3) {
-        scan(c + 2);
+        scan(c + 2, (m + 2) % 3);
         load_gates(c + 3);
       }
-      factors(c + 1);
+      factors(c + 1, (m + 1) % 3);
       __syncthreads();
+    };
+    for (int c = 0; c < nc; c += 3) {
+      step(c, std::integral_constant<int, 0>{});
+      if (c + 1 >= nc) break;
+      step(c + 1, std::integral_constant<int, 1>{});
+      if (c + 2 >= nc) break;
+      step(c + 2, std::integral_constant<int, 2>{});
     }
     };
     auto by_wave = [&](auto wo_c) __attribute__((always_inline)) {
