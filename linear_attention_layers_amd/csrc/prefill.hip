@@ -951,10 +951,14 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
 
       // The chain of the chunk is Z -> R -> the four block steps of the
       // solve -> the state update.  Each U block, once final, immediately
-      // feeds its share of the state update and of O.  The Q S0^T products
-      // are formed before the solve: between the block steps their fragment
-      // reads queued ahead of each step's own LDS reads (LDS returns in
-      // order) and lengthened the chain.
+      // feeds its share of the state update and of U P^T.  The Q S0^T
+      // products, which no later step of the chain needs, are formed after
+      // the state update: anywhere earlier their fragment reads queue ahead
+      // of the chain's own LDS reads (LDS returns in order) and their
+      // products ahead of its MFMAs (between the block steps, before the
+      // solve, and measured 2% slower there than here).  U P^T stays in
+      // the solve, where it fills the matrix pipe while a block step waits
+      // (3% slower after the update).
       // S0 is read as bf16 operands taken before the update (sb), so the
       // float32 state is updated in place.
 
@@ -1047,12 +1051,6 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       // between the two shapes that the compiler does not insert (the
       // second one read stale accumulator elements), so mixed-shape sums are
       // formed on separate accumulators and added.
-      if (WO) {
-        qs_step(0);
-        qs_step(1);
-        qs_step(2);
-        qs_step(3);
-      }
       f32x4 uu[VB][4], pu[VB][4];
       {
         const auto td = PR::lds16(ATc, LDT, r16, 0, kg);
@@ -1148,6 +1146,10 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       }
 
       if (WO) {
+        qs_step(0);
+        qs_step(1);
+        qs_step(2);
+        qs_step(3);
         // ---- O^T = (Q S0^T)^T diag(gamma) + U^T P^T; lane: token 16 ib + r16,
         // state rows v0 + 4 kg .. +3
         ro_prev = buf_rsrc(o + c0 * Hv * DK, o_on ? n * Hv * DK * 2 : 0);
