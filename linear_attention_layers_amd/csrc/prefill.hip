@@ -439,6 +439,15 @@ __device__ __forceinline__ int kq_at(int r, int g) {
   return 4 * (32 * r + (g ^ (4 * (r & 7) + 2 * ((r >> 3) & 1)))) + 8 * (r >> 4);
 }
 
+// Element position of column c in a row of the factor tiles (-A / T and P).
+// Within each 32-column group the two 4-column quads a 16x16x32 fragment
+// lane reads (columns 4q .. 4q+3 and 16 + 4q .. 16+4q+3) are stored side by
+// side, so that fragment is one 16-byte read, and a 16x16x16 fragment (one
+// quad) one 8-byte read.
+__device__ __forceinline__ constexpr int ft_pos(int c) {
+  return 32 * (c >> 5) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
+}
+
 struct __attribute__((aligned(16))) SmemWS {
   static constexpr int LDT = BT + 8;   // rows of 64 tokens (bf16)
   uint16_t K[3][kKQTile];
@@ -660,11 +669,12 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         }
       }
       if constexpr (WO)
-        *reinterpret_cast<u32x2*>(&sm.P[ab][i * LDT + j0]) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        *reinterpret_cast<u32x2*>(&sm.P[ab][i * LDT + ft_pos(j0)]) =
+            u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
       if constexpr (diag)
         *reinterpret_cast<float4*>(&sm.Ad[rw][r16][4 * kg]) = make_float4(av[0], av[1], av[2], av[3]);
       else
-        *reinterpret_cast<u32x2*>(&sm.AT[ab][i * LDT + j0]) =
+        *reinterpret_cast<u32x2*>(&sm.AT[ab][i * LDT + ft_pos(j0)]) =
             u32x2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
     };
     // this wave's tile pairs of K/Q buffer kb: (rw, rw) on the diagonal, the
@@ -720,8 +730,8 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       const int c = lane >> 2, qd = lane & 3, bb = rw;
       // row q + 4 m has nonzero entries only in columns j < q + 4 m <= 4 m + 3,
       // so its columns past 4 m + 2 are neither read nor applied (they are
-      // zero, and subtracting a zero product leaves x unchanged), and x_15
-      // feeds no row
+      // zero, and subtracting a zero product leaves x unchanged up to the
+      // sign of a zero), and x_15 feeds no row
       float arow[4][16];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -742,7 +752,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           if (j <= 4 * m + 2) x[m] = __builtin_fmaf(-arow[m][j], xj, x[m]);
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + 16 * bb + c], x[m]);
+      for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + ft_pos(16 * bb + c)], x[m]);
     };
     // all factors of chunk c (K/Q and gate buffer c % 3 -> factor buffer c & 1)
     auto factors = [&](int c, int kb) __attribute__((always_inline)) {
@@ -1051,15 +1061,37 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       // between the two shapes that the compiler does not insert (the
       // second one read stale accumulator elements), so mixed-shape sums are
       // formed on separate accumulators and added.
+      // fragments of the factor tiles (ft_pos layout): fr32 = columns
+      // 32 g .. 32 g + 31 of a 16x16x32 fragment (one 16-byte read), fr16 =
+      // columns 16 h .. 16 h + 15 of a 16x16x16 one (one 8-byte read)
+      // (the offset passes through an empty asm operand, which keeps the
+      // compiler from hoisting these reads ahead of the chain's own: LDS
+      // returns data in order)
+      auto fr32 = [&](const uint16_t* p, int row, int g) __attribute__((always_inline)) {
+        int off = row * LDT + 32 * g + 8 * kg;
+        asm volatile("" : "+v"(off));
+        typename PR::F32 f;
+        f.v = *reinterpret_cast<const uint4*>(p + off);
+        return f;
+      };
+      auto fr16 = [&](const uint16_t* p, int row, int h) __attribute__((always_inline)) {
+        int off = row * LDT + 32 * (h >> 1) + 8 * kg + 4 * (h & 1);
+        asm volatile("" : "+v"(off));
+        typename PR::F16 f;
+        f.v = *reinterpret_cast<const uint2*>(p + off);
+        return f;
+      };
+      auto lo16 = [](typename PR::F32 f) { typename PR::F16 r; r.v = make_uint2(f.v.x, f.v.y); return r; };
+      auto hi16 = [](typename PR::F32 f) { typename PR::F16 r; r.v = make_uint2(f.v.z, f.v.w); return r; };
       f32x4 uu[VB][4], pu[VB][4];
       {
-        const auto td = PR::lds16(ATc, LDT, r16, 0, kg);
+        const auto td = fr16(ATc, r16, 0);
 #pragma unroll
         for (int b = 0; b < VB; ++b) uu[b][0] = PR::mma16(td, PR::reg16(rr[b][0]), zero4());
       }
       {
-        const auto am = PR::lds16(ATc, LDT, 16 + r16, 0, kg);
-        const auto td = PR::lds16(ATc, LDT, 16 + r16, 16, kg);
+        const auto amtd = fr32(ATc, 16 + r16, 0);
+        const auto am = lo16(amtd), td = hi16(amtd);
 #pragma unroll
         for (int b = 0; b < VB; ++b) {
           rr[b][1] = PR::mma16(am, PR::reg16(uu[b][0]), rr[b][1]);
@@ -1081,20 +1113,20 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
           du[b] = PR::reg32(d0, d1);
           u01[b] = PR::reg32(uu[b][0], uu[b][1]);
         }
-        const auto a2 = PR::lds32(ATc, LDT, 32 + r16, 0, kg);
-        const auto a3 = PR::lds32(ATc, LDT, 48 + r16, 0, kg);
+        const auto a2 = fr32(ATc, 32 + r16, 0);
+        const auto a3 = fr32(ATc, 48 + r16, 0);
 #pragma unroll
         for (int b = 0; b < VB; ++b) {
           rr[b][2] = PR::mma32(a2, u01[b], rr[b][2]);
           rr[b][3] = PR::mma32(a3, u01[b], rr[b][3]);
         }
         if (WO) {
-          const auto p0 = PR::lds16(Pc, LDT, r16, 0, kg);
+          const auto p0 = fr16(Pc, r16, 0);
 #pragma unroll
           for (int b = 0; b < VB; ++b) pu[b][0] = PR::mma16(PR::reg16(uu[b][0]), p0, zero4());
 #pragma unroll
           for (int ib = 1; ib < 4; ++ib) {
-            const auto p01 = PR::lds32(Pc, LDT, 16 * ib + r16, 0, kg);
+            const auto p01 = fr32(Pc, 16 * ib + r16, 0);
 #pragma unroll
             for (int b = 0; b < VB; ++b) pu[b][ib] = PR::mma32(u01[b], p01, zero4());
           }
@@ -1102,13 +1134,13 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         state_half(0, du, true);
       }
       {
-        const auto td = PR::lds16(ATc, LDT, 32 + r16, 32, kg);
+        const auto td = fr16(ATc, 32 + r16, 2);
 #pragma unroll
         for (int b = 0; b < VB; ++b) uu[b][2] = PR::mma16(td, PR::reg16(rr[b][2]), zero4());
       }
       {
-        const auto am = PR::lds16(ATc, LDT, 48 + r16, 32, kg);
-        const auto td = PR::lds16(ATc, LDT, 48 + r16, 48, kg);
+        const auto amtd = fr32(ATc, 48 + r16, 1);
+        const auto am = lo16(amtd), td = hi16(amtd);
 #pragma unroll
         for (int b = 0; b < VB; ++b) {
           const f32x4 t3 = PR::mma16(am, PR::reg16(uu[b][2]), zero4());
@@ -1133,8 +1165,8 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         }
         state_half(32, du, false);
         if (WO) {
-          const auto p2 = PR::lds16(Pc, LDT, 32 + r16, 32, kg);
-          const auto p3 = PR::lds32(Pc, LDT, 48 + r16, 32, kg);
+          const auto p2 = fr16(Pc, 32 + r16, 2);
+          const auto p3 = fr32(Pc, 48 + r16, 1);
 #pragma unroll
           for (int b = 0; b < VB; ++b) {
             const f32x4 t2 = PR::mma16(PR::reg16(uu[b][2]), p2, zero4());
