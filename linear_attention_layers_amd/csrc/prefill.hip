@@ -931,7 +931,9 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     load_v(0);
     put_v(0);
     load_v(1);
-    __syncthreads();
+    // K, Q, the gates and V of chunk 0 are in LDS after this barrier; the
+    // producers form chunk 0's factors until the next one, which chunk 0's
+    // iteration takes just before its solve: Z and R overlap those factors
     __syncthreads();
 
     // The loop runs three chunks per trip so that the K / Q and gate buffer
@@ -1061,6 +1063,9 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       // between the two shapes that the compiler does not insert (the
       // second one read stale accumulator elements), so mixed-shape sums are
       // formed on separate accumulators and added.
+      if constexpr (kb == 0) {
+        if (c == 0) __syncthreads();   // chunk 0's factors are in LDS
+      }
       // fragments of the factor tiles (ft_pos layout): fr32 = columns
       // 32 g .. 32 g + 31 of a 16x16x32 fragment (one 16-byte read), fr16 =
       // columns 16 h .. 16 h + 15 of a 16x16x16 one (one 8-byte read)
