@@ -12,7 +12,10 @@
 //   O = diag(gamma) Q S0^T + P U,  P_ij = exp(G_i - G_j) (q_i . k_j) (j <= i)
 //   S = gamma_{n-1} S0 + (diag(d) U)^T K
 // (U = T diag(b) V - T diag(b gamma) K S0^T with T = (I + A)^-1 is the usual
-// WY factor; here it is reached by solving (I + A) U = R blockwise.)
+// WY factor; here it is reached by solving (I + A) U = R blockwise.  The bf16
+// kernel keeps b out of R: with A = diag(b) A~ it forms R~_i = v_i -
+// gamma_i Z_i and U_i = T'_ii (R~_i - sum_{j<i} A~_ij U_j), where T'_ii =
+// (I + A_ii)^-1 diag(b_i) and A~_ij = exp(G_i - G_j) (k_i . k_j).)
 //
 // Work split.  Rows of S (the dv index) evolve independently.  A workgroup
 // owns one (sequence, v-head, slice of state rows) and walks the sequence's
@@ -452,7 +455,7 @@ struct __attribute__((aligned(16))) SmemWS {
   static constexpr int LDT = BT + 8;   // rows of 64 tokens (bf16)
   uint16_t K[3][kKQTile];
   uint16_t Q[3][kKQTile];
-  uint16_t AT[2][BT * LDT];   // off-diagonal 16x16 blocks: -A; diagonal blocks: T_bb
+  uint16_t AT[2][BT * LDT];   // off-diagonal 16x16 blocks: -A~; diagonal blocks: T_bb diag(b)
   uint16_t P[2][BT * LDT];
   float W[3][4][BT];          // per chunk: log2-scaled G, gamma, beta, d
   float Ad[4][16][20];        // diagonal block of A of each producer wave
@@ -644,7 +647,9 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       Wc[2 * BT + lane] = br;
       Wc[3 * BT + lane] = lane < n ? __builtin_amdgcn_exp2f(Llast - L) : 0.f;
     };
-    // P and -A of tile pair (bi, bj), bi >= bj, from its products kk, qk:
+    // P and -A~ of tile pair (bi, bj), bi >= bj, from its products kk, qk
+    // (A~ without the row's beta, which the stored T_ii diag(beta) applies;
+    // the diagonal block keeps it, for the inverse):
     // lane (r16, kg) holds rows i = 16 bi + r16, columns j = 16 bj + 4 kg + e
     // (transposed products: K_bj-rows as the A operand)
     auto pair_store = [&](auto diag_c, int bi, int bj, f32x4 kk, f32x4 qk, int kb, int ab) __attribute__((always_inline)) {
@@ -665,7 +670,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         } else {
           const float dec = __builtin_amdgcn_exp2f(Li - lj[e]);
           pv[e] = dec * qk[e];
-          av[e] = bti * dec * kk[e];
+          av[e] = dec * kk[e];
         }
       }
       if constexpr (WO)
@@ -726,7 +731,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
     // q+8, q+12 of column c; the four lanes of a column form a DPP quad and
     // x_j, once final, is broadcast from the lane owning row j.  Terms with
     // j >= i vanish: A_bb is strictly lower triangular.
-    auto invert_diag = [&](int ab) {
+    auto invert_diag = [&](int ab, int kbw) {
       const int c = lane >> 2, qd = lane & 3, bb = rw;
       // row q + 4 m has nonzero entries only in columns j < q + 4 m <= 4 m + 3,
       // so its columns past 4 m + 2 are neither read nor applied (they are
@@ -751,14 +756,17 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         for (int m = 0; m < 4; ++m)
           if (j <= 4 * m + 2) x[m] = __builtin_fmaf(-arow[m][j], xj, x[m]);
       }
+      // stored as T_bb diag(beta): column c scaled by its token's beta, so
+      // the consumers' solve needs no beta
+      const float bc = sm.W[kbw][2][16 * bb + c];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + ft_pos(16 * bb + c)], x[m]);
+      for (int m = 0; m < 4; ++m) PR::put(&sm.AT[ab][(16 * bb + qd + 4 * m) * LDT + ft_pos(16 * bb + c)], x[m] * bc);
     };
     // all factors of chunk c (K/Q and gate buffer c % 3 -> factor buffer c & 1)
     auto factors = [&](int c, int kb) __attribute__((always_inline)) {
       const int ab = c & 1;
       pairs(kb, ab);
-      invert_diag(ab);
+      invert_diag(ab, kb);
     };
 
     load_kq(0);
@@ -975,14 +983,12 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
       // float32 state is updated in place.
 
       // gate vectors of this lane's rows (tokens 16 ib + 4 kg + e)
-      float gam4[4][4], b4[4][4], d4[4][4];
+      float gam4[4][4], d4[4][4];
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
         const float4 ga = *reinterpret_cast<const float4*>(&Wc[BT + 16 * ib + 4 * kg]);
-        const float4 bt = *reinterpret_cast<const float4*>(&Wc[2 * BT + 16 * ib + 4 * kg]);
         const float4 dd = *reinterpret_cast<const float4*>(&Wc[3 * BT + 16 * ib + 4 * kg]);
         gam4[ib][0] = ga.x; gam4[ib][1] = ga.y; gam4[ib][2] = ga.z; gam4[ib][3] = ga.w;
-        b4[ib][0] = bt.x; b4[ib][1] = bt.y; b4[ib][2] = bt.z; b4[ib][3] = bt.w;
         d4[ib][0] = dd.x; d4[ib][1] = dd.y; d4[ib][2] = dd.z; d4[ib][3] = dd.w;
       }
       typename PR::F32 sb[VB][4];
@@ -1015,14 +1021,15 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         }
       }
 
-      // ---- R = diag(beta) (V - diag(gamma) Z)
+      // ---- R~ = V - diag(gamma) Z (beta enters through the stored
+      // T_ii diag(beta))
       f32x4 rr[VB][4];
 #pragma unroll
       for (int b = 0; b < VB; ++b)
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rr[b][ib][e] = b4[ib][e] * (vv[b][ib][e] - gam4[ib][e] * z[b][ib][e]);
+          for (int e = 0; e < 4; ++e) rr[b][ib][e] = vv[b][ib][e] - gam4[ib][e] * z[b][ib][e];
 
       // (Q S0^T)^T (rows: state rows, columns: tokens), one 32-wide slice
       // of the contraction at a time
@@ -1057,8 +1064,8 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(
         }
       };
 
-      // ---- block solve (I + A) U = R, interleaved with the products that
-      // each finished block enables.  An accumulator is never carried from
+      // ---- block solve U_i = (T_ii diag(beta)) (R~_i - sum_{j<i} A~_ij U_j),
+      // interleaved with the products that each finished block enables.  An accumulator is never carried from
       // a 16x16x32 MFMA into a 16x16x16 one: the hardware needs wait states
       // between the two shapes that the compiler does not insert (the
       // second one read stale accumulator elements), so mixed-shape sums are
