@@ -4,7 +4,8 @@ the tiny float32 layer's step form, a float32 commit, a long chain of
 committed one-token steps, and empty sequences (with and without an
 initial state, stored buffers poisoned with NaN) through every entry point
 that writes a final state.  Every call goes through the C ABI; the
-reference is the CPU oracle."""
+reference is the CPU oracle, except for a batch cut into groups of
+consecutive sequences, which must give the bits of one launch."""
 import os
 
 import numpy as np
@@ -398,3 +399,65 @@ def test_batch_without_tokens_writes_only_zero_states(path):
     if path in ("step", "fused", "prefill"):
         assert torch.all(st[0].cpu() == 0)
         assert torch.equal(st[1].cpu(), st_in[1])
+
+
+# ------------------------------------------------ a batch cut into groups
+
+SPLIT_LENGTHS = [300, 70, 0, 1, 129, 64, 500, 17]
+SPLIT_INIT = [1, 0, 1, 1, 0, 1, 1, 0]
+SPLIT_GROUPS = [(0, 2), (2, 5), (5, 8)]
+
+
+@pytest.mark.parametrize("path", ["convpost", "prefill", "segmented", "step"])
+def test_batch_split_into_consecutive_groups_equals_one_launch(path):
+    """A batch cut into runs of consecutive sequences, each run launched on
+    views of its own token rows, conv rows, states and flags with
+    cu_seqlens rebased to its first token, gives the bits of one launch over
+    the whole batch: a sequence's results depend on its own tokens and
+    states only, not on the batch around it."""
+    geo = I.Geometry(Hk=2, Hv=4)
+    lb = I.make_layer(geo, SPLIT_LENGTHS, "bf16", 1840, state_std=0.3, has_init=SPLIT_INIT)
+    Hk, Hv = geo.Hk, geo.Hv
+    cuh = lb.cu_seqlens.tolist()
+    x, w = lb.x.to(DEV), lb.conv_w.to(DEV)
+    cu, hi = lb.cu_seqlens.to(DEV), lb.has_init.to(DEV)
+    g, beta = lb.g.to(DEV).contiguous(), lb.beta.to(DEV).contiguous()
+    cs0, st0 = lb.conv_state.to(DEV).contiguous(), lb.state.to(DEV).contiguous()
+    q, k, v = gdn.gdn_conv_postconv_fwd(x, w, None, cs0.clone(), hi, cu, None, True, Hk, Hv, 1e-6)
+
+    def launch(cu_, hi_, cs, st, x_, q_, k_, v_, g_, b_, o_):
+        if path == "convpost":
+            gdn.gdn_conv_postconv_fwd(x_, w, None, cs, hi_, cu_, None, True, Hk, Hv, 1e-6, q=q_, k=k_, v=v_)
+        elif path == "prefill":
+            gdn.gdn_delta_rule_prefill(q_, k_, v_, g_, b_, cu_, st, hi_, o=o_)
+        elif path == "segmented":
+            gdn.gdn_delta_rule_prefill_segmented(q_, k_, v_, g_, b_, cu_, st, 3, hi_, o=o_)
+        else:
+            gdn.gdn_delta_rule_step(q_, k_, v_, g_, b_, cu_, st, hi_, o=o_, commit_state=True)
+
+    def outputs():
+        if path == "convpost":
+            return (torch.full_like(q, float("nan")), torch.full_like(k, float("nan")),
+                    torch.full_like(v, float("nan")))
+        return q, k, v
+
+    print(f"batch split: {path}", flush=True)
+    whole_cs, whole_st, whole_o = cs0.clone(), st0.clone(), torch.full_like(v, float("nan"))
+    wq, wk, wv = outputs()
+    launch(cu, hi, whole_cs, whole_st, x, wq, wk, wv, g, beta, whole_o)
+    part_cs, part_st, part_o = cs0.clone(), st0.clone(), torch.full_like(v, float("nan"))
+    pq, pk, pv = outputs()
+    for s0, s1 in SPLIT_GROUPS:
+        t0, t1 = cuh[s0], cuh[s1]
+        cug = (cu[s0:s1 + 1] - t0).contiguous()
+        launch(cug, hi[s0:s1], part_cs[s0:s1], part_st[s0:s1], x[t0:t1], pq[t0:t1], pk[t0:t1], pv[t0:t1],
+               g[t0:t1], beta[t0:t1], part_o[t0:t1])
+    torch.cuda.synchronize()
+    if path == "convpost":
+        for a, b, nm in ((wq, pq, "q"), (wk, pk, "k"), (wv, pv, "v")):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), nm
+        assert torch.equal(whole_cs.view(torch.int32), part_cs.view(torch.int32)), "conv_state"
+    else:
+        assert torch.equal(whole_o.view(torch.int16), part_o.view(torch.int16)), "o"
+        assert torch.equal(whole_st.view(torch.int32), part_st.view(torch.int32)), "state"
+        assert torch.isfinite(whole_o.float()).all()
