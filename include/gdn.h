@@ -45,7 +45,11 @@
  *     reads k-head h / (Hv/Hk).
  *   - Varlen batches: cu_seqlens[nseq+1] (device, int32) with cu[0] = 0,
  *     nondecreasing, cu[nseq] = N.  Device-resident integers are
- *     preconditions: they are not read back on the host.
+ *     preconditions: they are not read back on the host.  Sequences are
+ *     independent: a run of consecutive sequences [s0, s1) can be passed as
+ *     its own batch (token pointers advanced by cu[s0] rows, per-sequence
+ *     pointers by s0 entries, cu rebased to start at 0), and gives the same
+ *     bits as the whole batch.
  *   - has_initial_state[nseq] (device, uint8; NULL = all set): when 0, the
  *     sequence starts from zero conv rows and a zero recurrent state, and
  *     the stored buffers are not read (they may hold anything, NaN included).
