@@ -408,7 +408,7 @@ SPLIT_INIT = [1, 0, 1, 1, 0, 1, 1, 0]
 SPLIT_GROUPS = [(0, 2), (2, 5), (5, 8)]
 
 
-@pytest.mark.parametrize("path", ["convpost", "prefill", "segmented", "step"])
+@pytest.mark.parametrize("path", ["conv", "convpost", "prefill", "segmented", "step", "fused"])
 def test_batch_split_into_consecutive_groups_equals_one_launch(path):
     """A batch cut into runs of consecutive sequences, each run launched on
     views of its own token rows, conv rows, states and flags with
@@ -426,7 +426,12 @@ def test_batch_split_into_consecutive_groups_equals_one_launch(path):
     q, k, v = gdn.gdn_conv_postconv_fwd(x, w, None, cs0.clone(), hi, cu, None, True, Hk, Hv, 1e-6)
 
     def launch(cu_, hi_, cs, st, x_, q_, k_, v_, g_, b_, o_):
-        if path == "convpost":
+        if path == "conv":   # y (in q_'s place) with the chunk list of this batch
+            gdn.gdn_causal_conv_fwd(x_, w, None, cs, hi_, cu_, gdn.gdn_make_chunks_device(cu_, x_.shape[0]), True,
+                                    y=q_)
+        elif path == "fused":
+            gdn.gdn_decode_fused(x_, w, None, cs, cu_, g_, b_, st, Hk, Hv, 1e-6, hi_, o=o_)
+        elif path == "convpost":
             gdn.gdn_conv_postconv_fwd(x_, w, None, cs, hi_, cu_, None, True, Hk, Hv, 1e-6, q=q_, k=k_, v=v_)
         elif path == "prefill":
             gdn.gdn_delta_rule_prefill(q_, k_, v_, g_, b_, cu_, st, hi_, o=o_)
@@ -436,6 +441,8 @@ def test_batch_split_into_consecutive_groups_equals_one_launch(path):
             gdn.gdn_delta_rule_step(q_, k_, v_, g_, b_, cu_, st, hi_, o=o_, commit_state=True)
 
     def outputs():
+        if path == "conv":
+            return torch.full_like(x, float("nan")), None, None
         if path == "convpost":
             return (torch.full_like(q, float("nan")), torch.full_like(k, float("nan")),
                     torch.full_like(v, float("nan")))
@@ -450,14 +457,18 @@ def test_batch_split_into_consecutive_groups_equals_one_launch(path):
     for s0, s1 in SPLIT_GROUPS:
         t0, t1 = cuh[s0], cuh[s1]
         cug = (cu[s0:s1 + 1] - t0).contiguous()
-        launch(cug, hi[s0:s1], part_cs[s0:s1], part_st[s0:s1], x[t0:t1], pq[t0:t1], pk[t0:t1], pv[t0:t1],
+        cut = (lambda t: None if t is None else t[t0:t1])
+        launch(cug, hi[s0:s1], part_cs[s0:s1], part_st[s0:s1], x[t0:t1], cut(pq), cut(pk), cut(pv),
                g[t0:t1], beta[t0:t1], part_o[t0:t1])
     torch.cuda.synchronize()
-    if path == "convpost":
-        for a, b, nm in ((wq, pq, "q"), (wk, pk, "k"), (wv, pv, "v")):
-            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), nm
+    if path in ("conv", "convpost"):
+        for a, b, nm in ((wq, pq, "q / y"), (wk, pk, "k"), (wv, pv, "v")):
+            if a is not None:
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), nm
         assert torch.equal(whole_cs.view(torch.int32), part_cs.view(torch.int32)), "conv_state"
     else:
+        if path == "fused":
+            assert torch.equal(whole_cs.view(torch.int32), part_cs.view(torch.int32)), "conv_state"
         assert torch.equal(whole_o.view(torch.int16), part_o.view(torch.int16)), "o"
         assert torch.equal(whole_st.view(torch.int32), part_st.view(torch.int32)), "state"
         assert torch.isfinite(whole_o.float()).all()
