@@ -29,9 +29,10 @@ Prints ONE JSON line: throughput in layer-tokens/s, the roofline of the
 dominant kernel (its per-launch HIP-event time inside the timed region, on
 the stream it runs on; the warm-up steps, timed per launch, pick it by their
 median), every kernel's time from an instrumented pass after the timed
-region, the CPU oracle timed on a bounded sample of the same workload over a
-pool of host processes, and a
-cold-cache pass (`cold_cache`: up to 20 more steps, each after a 1 GiB read
+region (with each one's fraction of a plain device copy's bandwidth,
+`copy_bandwidth`, measured after the timed region as context), the CPU
+oracle timed on a bounded sample of the same workload over a pool of host
+processes, and a cold-cache pass (`cold_cache`: up to 20 more steps, each after a 1 GiB read
 that evicts L2 and the Infinity Cache, timed with events; context beside
 `value`, which is the warm timed region).
 
@@ -801,6 +802,33 @@ def cold_pass(runner, reps):
             "steps": reps, "flush_bytes": 1 << 30, "stages": stages}
 
 
+def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """A plain device-to-device copy of nbytes (torch's copy kernel), timed
+    with events after two untimed copies: bytes read and written over the
+    median time.  Context for the stages' HBM fractions: a kernel that
+    streams its bytes once gets about this far on the same GPU."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) / 1e3)
+    del src, dst
+    t = sorted(ts)[len(ts) // 2]
+    gbs = 2 * nbytes / t / 1e9
+    return {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_moved": 2 * nbytes,
+            "kernel": "torch copy_ of 1 GiB on one device (hipMemcpyAsync, the HIP runtime's copy kernel), "
+                      "median of 10"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -916,6 +944,7 @@ def main():
 
     ms_per_step = wall * 1e3 / steps
     tokens_per_s = plan.tokens / (ms_per_step / 1e3)
+    copy_bw = copy_bandwidth(dev)
     stages = {}
     for nm in names:
         t = per_step_ms[nm] / 1e3
@@ -924,6 +953,7 @@ def main():
         if plan.bytes.get(nm):
             rec["GB/s"] = round(plan.bytes[nm] / t / 1e9, 1)
             rec["hbm_frac"] = round(plan.bytes[nm] / t / 1e9 / HBM_PEAK_GBS, 4)
+            rec["of_copy"] = round(plan.bytes[nm] / t / 1e9 / copy_bw["GB/s"], 4)
         if plan.flops.get(nm):
             tf = plan.flops[nm] / t / 1e12
             rec["mfma_TFLOP/s"] = round(tf, 2)
@@ -966,6 +996,7 @@ def main():
         "config": plan.config,
         "roofline": roofline,
         "stages": stages,
+        "copy_bandwidth": copy_bw,
     }
     if not args.no_cold:
         out["cold_cache"] = cold_pass(runner, min(steps, 20))
