@@ -657,25 +657,25 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
   if (commit_state) store_state(base, v0, r16, kg, st);
 
   // conv_state <- the last 3 rows of [stored rows ; x window] for this
-  // workgroup's channels.  Each lane reads all three final rows of its
-  // channels before writing any, so a row shifted down from a stored row is
-  // read and written by the same lane, in program order.
+  // workgroup's channels, read from LDS: the last block's staged x rows
+  // (row r = block token r - 3) hold every final token, and the staged
+  // stored rows (zeros without an initial state) the rows before the
+  // sequence when it has fewer than 3 tokens.
   if (write_conv_state && a_row && wave == 0) {
     const int cg = chan(hs * 128 + 8 * jl);
+    const int ca = hs * 128 + 8 * jl;
+    const int c_last = (len - 1) / kWin * kWin;   // first token of the last block
     float v8[3][8];
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
       const int tr = len - 3 + r;   // token index of final row r
       if (tr >= 0) {
-        Act<T>::load8(x + (int64_t)(bos + tr) * xs + cg, v8[r]);
-      } else if (init) {
-        const float* p = cs + (int64_t)(3 + tr) * C + cg;
-        const float4 a = *reinterpret_cast<const float4*>(p), b4 = *reinterpret_cast<const float4*>(p + 4);
+        Act<T>::load8(&sm.Xs[(tr - c_last + 3) * CH + ca], v8[r]);
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(&sm.Cs[(3 + tr) * CH + ca]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&sm.Cs[(3 + tr) * CH + ca + 4]);
         v8[r][0] = a.x; v8[r][1] = a.y; v8[r][2] = a.z; v8[r][3] = a.w;
         v8[r][4] = b4.x; v8[r][5] = b4.y; v8[r][6] = b4.z; v8[r][7] = b4.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v8[r][i] = 0.f;
       }
     }
 #pragma unroll
