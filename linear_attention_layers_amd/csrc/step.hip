@@ -421,7 +421,12 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_ker
 // Load order.  One in-order counter covers a wave's vector memory
 // operations, so the first block's staged rows, the conv weights and the
 // gates are requested before the state: phase A then waits only for them
-// while the state is still arriving.
+// while the state is still arriving.  With every workgroup asking for its
+// state at once, issuing the state reads is itself paced by the memory
+// system, and a wave runs nothing placed after a read before that read is
+// issued; so half of the state is requested before phase A and half after
+// it, and phase A issues no global stores (the k and v kept for a commit
+// are copied out of the tiles after phase B).
 template <class T, int G> struct alignas(16) FusedSmem {
   using E = typename Prec<T>::E;
   static constexpr int LDK = 128 + Prec<T>::PAD;
@@ -569,14 +574,34 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
   };
   load_gates(0, n);
 
+  // The state is requested in two halves, the second after the first
+  // block's conv and post-conv phase: issuing the reads is paced by the
+  // memory system (every workgroup asks for its state at once), and a
+  // wave runs nothing placed after a read before that read is issued.
   f32x4 st[kRB][8];
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
-  load_state(base, init, v0, r16, kg, st);
+  const auto rs = buf_rsrc(base, init ? 128 * 128 * 4 : 0);
+  // (the row block's offset is wave-uniform and goes in the scalar offset,
+  // so every read takes the same lane offset plus an immediate)
+  auto load_state_rows = [&](int b0, int b1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = b0; b < b1; ++b)
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+        st[b][cb] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r16 * 128 + 16 * cb + 4 * kg) * 4,
+                                                         __builtin_amdgcn_readfirstlane((v0 + 16 * b) * 512), 0));
+  };
+  load_state_rows(0, kRB / 2);
   write_stage(0);   // waits for the staged pieces only
 
-  for (int c0 = 0; c0 < len; c0 += kWin) {
+  // one block of the window; the first is peeled (a compile-time flag), so
+  // the second half of the state reads is issued on every path through it
+  // and no merged wait count covers it early
+  auto one_block = [&](int c0, auto first_c) __attribute__((always_inline)) {
+    constexpr bool first = decltype(first_c)::value;
     n = min(kWin, len - c0);
-    if (c0 > 0) {
+    if constexpr (!first) {
       issue_stage(c0, n);
       load_gates(c0, n);
       write_stage(c0);
@@ -602,7 +627,7 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
           for (int r = 0; r < 4; ++r) {
             const int sr = t + r;
             float xr[8];
-            if (c0 == 0 && sr < 3) {
+            if (first && sr < 3) {
               const float4 a = *reinterpret_cast<const float4*>(&sm.Cs[sr * CH + ca]);
               const float4 b4 = *reinterpret_cast<const float4*>(&sm.Cs[sr * CH + ca + 4]);
               xr[0] = a.x; xr[1] = a.y; xr[2] = a.z; xr[3] = a.w;
@@ -626,10 +651,6 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
           }
           Act<T>::unpack(ry, yv);
           postconv_lane<T>(yv, hs < 2, eps, out);
-          // the normalised k and the v kept for a later commit's replay
-          const int64_t tg = (int64_t)bos + c0 + t;
-          if (hs == 1 && k_out != nullptr) Act<T>::store8(k_out + (tg * Hk + kh) * 128 + 8 * jl, out);
-          if (hs >= 2 && v_out != nullptr) Act<T>::store8(v_out + (tg * Hv + kh * G + hs - 2) * 128 + 8 * jl, out);
         } else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) out[i] = 0.f;
@@ -638,6 +659,7 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
         Act<T>::store8(dst + t * LDK + 8 * jl, out);
       }
     }
+    if constexpr (first) load_state_rows(kRB / 2, kRB);
     __syncthreads();
 
     // phase B: the step's block on this v-head group's waves
@@ -652,8 +674,28 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
       for (int e = 0; e < 4; ++e) in.vv[b][e] = PR::to_f32(sm.Vs[grp][(4 * kg + e) * LDK + v0 + 16 * b + r16]);
     run_block<T, true>(sm.w[wave], sm.Ks, sm.Qs, wl, lane, st, in, o, Hv, h,
                        commit_state != 0 || c0 + kWin < len);
+    // the normalised k and the v kept for a later commit's replay, copied
+    // from the tiles (the values phase A wrote there) once the block's
+    // state reads are out of the way
+    if (k_out != nullptr || v_out != nullptr) {
+      constexpr int PR16 = 128 / PE;              // 16-byte pieces per row
+      for (int i = tid; i < (1 + G) * n * PR16; i += NT) {
+        const int hh = i / (n * PR16), rem = i % (n * PR16), t = rem / PR16, c = (rem % PR16) * PE;
+        const int64_t tg = (int64_t)bos + c0 + t;
+        if (hh == 0) {
+          if (k_out != nullptr)
+            *reinterpret_cast<uint4*>(k_out + (tg * Hk + kh) * 128 + c) =
+                *reinterpret_cast<const uint4*>(&sm.Ks[t * LDK + c]);
+        } else if (v_out != nullptr) {
+          *reinterpret_cast<uint4*>(v_out + (tg * Hv + kh * G + hh - 1) * 128 + c) =
+              *reinterpret_cast<const uint4*>(&sm.Vs[hh - 1][t * LDK + c]);
+        }
+      }
+    }
     __syncthreads();
-  }
+  };
+  one_block(0, std::true_type{});
+  for (int c0 = kWin; c0 < len; c0 += kWin) one_block(c0, std::false_type{});
   if (commit_state) store_state(base, v0, r16, kg, st);
 
   // conv_state <- the last 3 rows of [stored rows ; x window] for this
