@@ -72,19 +72,23 @@ template <class T> struct alignas(16) StepSmem {
   WaveScratch<T> w[kStepWaves];
 };
 
-// S^T of rows v0 + 16 b + r16 in accumulator layout: tile cb holds
-// S[v0 + 16 b + r16][16 cb + 4 kg + e].  Read through a buffer resource
-// that spans the state, or nothing (all zeros) when there is no initial
-// state, so the read is branch-free.
-__device__ __forceinline__ void load_state(const float* base, bool init, int v0, int r16, int kg,
-                                           f32x4 (&st)[kRB][8]) {
-  const auto rs = buf_rsrc(base, init ? 128 * 128 * 4 : 0);
+// S^T of rows v0 + 16 b + r16, b0 <= b < b1, in accumulator layout: tile
+// cb holds S[v0 + 16 b + r16][16 cb + 4 kg + e].  rs spans the state, or
+// nothing (all zeros) when there is no initial state, so the read is
+// branch-free.  The row block's offset is wave-uniform and goes in the
+// scalar offset, so every read takes one lane offset plus an immediate.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float* base, bool init) {
+  return buf_rsrc(base, init ? 128 * 128 * 4 : 0);
+}
+__device__ __forceinline__ void load_state_rows(__amdgpu_buffer_rsrc_t rs, int v0, int r16, int kg,
+                                                f32x4 (&st)[kRB][8], int b0, int b1) {
 #pragma unroll
-  for (int b = 0; b < kRB; ++b)
+  for (int b = b0; b < b1; ++b)
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
       st[b][cb] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ((v0 + 16 * b + r16) * 128 + 16 * cb + 4 * kg) * 4, 0, 0));
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r16 * 128 + 16 * cb + 4 * kg) * 4,
+                                                       __builtin_amdgcn_readfirstlane((v0 + 16 * b) * 512), 0));
 }
 
 __device__ __forceinline__ void store_state(float* base, int v0, int r16, int kg, const f32x4 (&st)[kRB][8]) {
@@ -166,11 +170,15 @@ __device__ __forceinline__ void stage_block(typename Prec<T>::E* Ks, typename Pr
 // row stride LDK); `wave` selects the state rows 32 wave .. 32 wave + 31.
 // K and Q fragments are read from the tiles where they are used, so they
 // are not held in registers next to the state.
-template <class T, bool WITH_O>
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+template <class T, bool WITH_O, class Mid = NoMid>
 __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Prec<T>::E* Ks,
                                           const typename Prec<T>::E* Qs, int wave, int lane,
                                           f32x4 (&st)[kRB][8], const BlockIn<T, WITH_O>& in, T* o,
-                                          int Hv, int h, bool advance) {
+                                          int Hv, int h, bool advance, Mid mid = Mid{}) {
   using PR = Prec<T>;
   using E = typename PR::E;
   constexpr int ES = sizeof(E);
@@ -250,6 +258,9 @@ __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Pre
     for (int m = 0; m < 4; ++m) PR::put(&Tm[(qd + 4 * m) * LDT + c], x[m]);
   }
   const auto tf = PR::lds16(Tm, LDT, r16, 0, kg);
+  // everything above is the token side; a caller may issue work here that
+  // must come after it in program order (the rest of its state reads)
+  mid();
 
   // Z = K S0^T (rows: tokens) and (Q S0^T)^T (rows: state rows).  With bf16
   // operands the float32 state enters as hi + lo (two products each): one
@@ -341,16 +352,16 @@ __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Pre
 // already requested by the caller (with the state), so a unit's loads are
 // in flight together.  WITH_O writes o; the state is advanced over every
 // block except, when !write_state, the last.
-template <class T, bool WITH_O>
+template <class T, bool WITH_O, class Mid = NoMid>
 __device__ __forceinline__ void run_window(StepSmem<T>& sm, int wave, int lane, f32x4 (&st)[kRB][8],
                                            BlockIn<T, WITH_O>& in, const T* q, const T* k,
                                            const T* v, const float* g, const float* beta, T* o,
                                            int bos, int len, int Hk, int Hv, int h, int kh,
-                                           bool write_state) {
+                                           bool write_state, Mid mid = Mid{}) {
   const int v0 = kRows * wave;
   stage_block<T, WITH_O>(sm.K, sm.Q, in, wave, lane);
   __syncthreads();
-  run_block<T, WITH_O>(sm.w[wave], sm.K, sm.Q, wave, lane, st, in, o, Hv, h, write_state || len > kWin);
+  run_block<T, WITH_O>(sm.w[wave], sm.K, sm.Q, wave, lane, st, in, o, Hv, h, write_state || len > kWin, mid);
   for (int c0 = kWin; c0 < len; c0 += kWin) {
     load_block<T, WITH_O>(in, lane, wave, q, k, v, g, beta, (int64_t)bos + c0, min(kWin, len - c0), Hk,
                           Hv, h, kh, v0);
@@ -390,14 +401,24 @@ __global__ __launch_bounds__(kStepThreads, sizeof(T) == 2 ? 2 : 1) void step_ker
   }
   BlockIn<T, true> in;
   load_block<T, true>(in, lane, wave, q, k, v, g, beta, bos, min(kWin, len), Hk, Hv, h, kh, v0);
+  // The state (zeros without an initial state) is requested in two halves,
+  // the second between the first block's token side and its state side:
+  // with every workgroup asking for its state at once, issuing the reads is
+  // paced by the memory system, and a wave runs nothing placed after a
+  // read before that read is issued.
   f32x4 st[kRB][8];
-  load_state(base, init, v0, r16, kg, st);   // zeros without an initial state
-  // every state read is issued before anything uses one: the scheduler
-  // would otherwise hoist the first block's conversions between the reads,
-  // and the in-order wait for them would hold back the remaining reads
+  const auto rs = state_rsrc(base, init);
+  load_state_rows(rs, v0, r16, kg, st, 0, kRB / 2);
+  // the first half is issued before anything uses a read: the scheduler
+  // would otherwise hoist the block's conversions between the reads, and
+  // the in-order wait for them would hold back the remaining reads
   __builtin_amdgcn_sched_barrier(0);
   run_window<T, true>(sm, wave, lane, st, in, q, k, v, g, beta, o, bos, len, Hk, Hv, h, kh,
-                      commit_state != 0);
+                      commit_state != 0, [&]() __attribute__((always_inline)) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        load_state_rows(rs, v0, r16, kg, st, kRB / 2, kRB);
+                        __builtin_amdgcn_sched_barrier(0);
+                      });
   if (commit_state) store_state(base, v0, r16, kg, st);
 }
 
@@ -580,19 +601,8 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
   // wave runs nothing placed after a read before that read is issued.
   f32x4 st[kRB][8];
   float* base = state + ((int64_t)s * Hv + h) * (128 * 128);
-  const auto rs = buf_rsrc(base, init ? 128 * 128 * 4 : 0);
-  // (the row block's offset is wave-uniform and goes in the scalar offset,
-  // so every read takes the same lane offset plus an immediate)
-  auto load_state_rows = [&](int b0, int b1) __attribute__((always_inline)) {
-#pragma unroll
-    for (int b = b0; b < b1; ++b)
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb)
-        st[b][cb] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r16 * 128 + 16 * cb + 4 * kg) * 4,
-                                                         __builtin_amdgcn_readfirstlane((v0 + 16 * b) * 512), 0));
-  };
-  load_state_rows(0, kRB / 2);
+  const auto rs = state_rsrc(base, init);
+  load_state_rows(rs, v0, r16, kg, st, 0, kRB / 2);
   write_stage(0);   // waits for the staged pieces only
 
   // one block of the window; the first is peeled (a compile-time flag), so
@@ -659,7 +669,7 @@ __global__ __launch_bounds__(kStepThreads * G, sizeof(T) == 2 ? 2 : 1) void fuse
         Act<T>::store8(dst + t * LDK + 8 * jl, out);
       }
     }
-    if constexpr (first) load_state_rows(kRB / 2, kRB);
+    if constexpr (first) load_state_rows(rs, v0, r16, kg, st, kRB / 2, kRB);
     __syncthreads();
 
     // phase B: the step's block on this v-head group's waves
@@ -759,11 +769,18 @@ __global__ __launch_bounds__(kStepThreads, 1) void commit_kernel(
     BlockIn<T, false> in;
     load_block<T, false>(in, lane, wave, nullptr, static_cast<const T*>(io.k), static_cast<const T*>(io.v), io.g,
                          io.beta, bos, min(kWin, n), Hk, Hv, h, kh, kRows * wave);
-    load_state(base, init, kRows * wave, r16, kg, st);
-    __builtin_amdgcn_sched_barrier(0);   // all state reads issued before any use
+    // the state in two halves around the first block's token side, as in
+    // the step
+    const auto rs = state_rsrc(base, init);
+    load_state_rows(rs, kRows * wave, r16, kg, st, 0, kRB / 2);
+    __builtin_amdgcn_sched_barrier(0);   // the first half issued before any use
     run_window<T, false>(sm, wave, lane, st, in, nullptr, static_cast<const T*>(io.k),
                          static_cast<const T*>(io.v), io.g, io.beta, nullptr, bos, n, Hk, Hv, h, kh,
-                         true);
+                         true, [&]() __attribute__((always_inline)) {
+                           __builtin_amdgcn_sched_barrier(0);
+                           load_state_rows(rs, kRows * wave, r16, kg, st, kRB / 2, kRB);
+                           __builtin_amdgcn_sched_barrier(0);
+                         });
     store_state(base, kRows * wave, r16, kg, st);
   } else {
     const int c0 = ((role - Hv) * kStepThreads + threadIdx.x) * 8;
