@@ -165,14 +165,17 @@ __device__ __forceinline__ void stage_block(typename Prec<T>::E* Ks, typename Pr
   }
 }
 
-// One block of a window: o of its tokens (WITH_O) and, when `advance`, the
-// state moved past them.  Ks / Qs hold the block's K and Q rows (16 x 128,
-// row stride LDK); `wave` selects the state rows 32 wave .. 32 wave + 31.
-// K and Q fragments are read from the tiles where they are used, so they
-// are not held in registers next to the state.
 struct NoMid {
   __device__ void operator()() const {}
 };
+
+// One block of a window: o of its tokens (WITH_O) and, when `advance`, the
+// state moved past them.  Ks / Qs hold the block's K and Q rows (16 x 128,
+// row stride LDK); `wave` selects the state rows kRows wave .. kRows wave +
+// kRows - 1.  K and Q fragments are read from the tiles where they are
+// used, so they are not held in registers next to the state.  `mid` runs
+// between the token side (gate vectors, K K^T, Q K^T, A, T) and the state
+// side, which reads st: a caller issues the rest of its state reads there.
 
 template <class T, bool WITH_O, class Mid = NoMid>
 __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Prec<T>::E* Ks,
@@ -348,10 +351,11 @@ __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Pre
 }
 
 // Runs tokens [bos, bos + len) of one (sequence, v-head) through this
-// wave's 32 state rows in st; `in` holds the first block's token inputs,
-// already requested by the caller (with the state), so a unit's loads are
-// in flight together.  WITH_O writes o; the state is advanced over every
-// block except, when !write_state, the last.
+// wave's kRows state rows in st; `in` holds the first block's token inputs,
+// already requested by the caller (with the state, or with its first part:
+// `mid` is the first block's, where the caller requests the rest), so a
+// unit's loads are in flight together.  WITH_O writes o; the state is
+// advanced over every block except, when !write_state, the last.
 template <class T, bool WITH_O, class Mid = NoMid>
 __device__ __forceinline__ void run_window(StepSmem<T>& sm, int wave, int lane, f32x4 (&st)[kRB][8],
                                            BlockIn<T, WITH_O>& in, const T* q, const T* k,
