@@ -860,7 +860,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the GDN hot path shards by sequence and head group with no exchange; "
-              "multi-GPU runs are not part of this build)", file=sys.stderr)
+              "this benchmark measures the one-GPU share only)", file=sys.stderr)
         sys.exit(2)
     default_steps = {"varlen": 100, "verify": 20, "long": 20, "mixed": 40, "verify-fused": 20,
                      "mixed-unfused": 20, "out-norm": 20, "gates": 20, "long-seg": 20}[args.workload]
