@@ -472,3 +472,53 @@ def test_batch_split_into_consecutive_groups_equals_one_launch(path):
         assert torch.equal(whole_o.view(torch.int16), part_o.view(torch.int16)), "o"
         assert torch.equal(whole_st.view(torch.int32), part_st.view(torch.int32)), "state"
         assert torch.isfinite(whole_o.float()).all()
+
+
+# ------------------------------------------ batches of more than 64 sequences
+
+def test_batch_of_70_sequences():
+    """70 sequences: past 64 the prefill runs them in index order instead
+    of longest first, and the conv + post-conv needs chunk descriptors.
+    The prefill is checked against the per-token oracle, and both launches
+    must give the bits of the same batch cut into two runs of 35 sequences
+    (the longest-first prefill and the in-launch chunk derivation)."""
+    geo = I.Geometry(Hk=1, Hv=2)
+    rng = np.random.default_rng(1870)
+    lengths = [int(v) for v in rng.choice([0, 1, 2, 17, 63, 64, 65, 130], size=70)]
+    hinit = [int(v) for v in rng.integers(0, 2, size=70)]
+    lb = I.make_layer(geo, lengths, "bf16", 1870, state_std=0.3, has_init=hinit)
+    Hk, Hv = geo.Hk, geo.Hv
+    cuh = lb.cu_seqlens.tolist()
+    x, w = lb.x.to(DEV), lb.conv_w.to(DEV)
+    cu, hi = lb.cu_seqlens.to(DEV), lb.has_init.to(DEV)
+    g, beta = lb.g.to(DEV).contiguous(), lb.beta.to(DEV).contiguous()
+    cs0, st0 = lb.conv_state.to(DEV).contiguous(), lb.state.to(DEV).contiguous()
+    print(f"70 sequences: {lb.N} tokens", flush=True)
+
+    # whole batch: conv + post-conv with descriptors, then the prefill
+    cs_w, st_w = cs0.clone(), st0.clone()
+    q, k, v = gdn.gdn_conv_postconv_fwd(x, w, None, cs_w, hi, cu, gdn.gdn_make_chunks_device(cu, lb.N), True,
+                                        Hk, Hv, 1e-6)
+    o = gdn.gdn_delta_rule_prefill(q, k, v, g, beta, cu, st_w, hi)
+    # two runs of 35 sequences (each on its own views, cu rebased)
+    cs_p, st_p = cs0.clone(), st0.clone()
+    qp, kp, vp = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    op = torch.full_like(o, float("nan"))
+    for s0, s1 in ((0, 35), (35, 70)):
+        t0, t1 = cuh[s0], cuh[s1]
+        cug = (cu[s0:s1 + 1] - t0).contiguous()
+        gdn.gdn_conv_postconv_fwd(x[t0:t1], w, None, cs_p[s0:s1], hi[s0:s1], cug, None, True, Hk, Hv, 1e-6,
+                                  q=qp[t0:t1], k=kp[t0:t1], v=vp[t0:t1])
+        gdn.gdn_delta_rule_prefill(qp[t0:t1], kp[t0:t1], vp[t0:t1], g[t0:t1], beta[t0:t1], cug, st_p[s0:s1],
+                                   hi[s0:s1], o=op[t0:t1])
+    torch.cuda.synchronize()
+    for a, b, nm in ((q, qp, "q"), (k, kp, "k"), (v, vp, "v"), (o, op, "o")):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), nm
+    assert torch.equal(cs_w.view(torch.int32), cs_p.view(torch.int32)), "conv_state"
+    assert torch.equal(st_w.view(torch.int32), st_p.view(torch.int32)), "state"
+
+    o_ref, st_ref = O.delta_rule_recurrent(TL.np64(q), TL.np64(k), TL.np64(v), TL.np64(lb.g),
+                                           TL.np64(lb.beta), TL.np64(lb.state), lb.has_init.numpy(),
+                                           cuh, Hk, Hv)
+    TL.check_normwise(TL.np64(o), o_ref, TL.REC_BF16, axes=(2,), what="o")
+    TL.check_normwise(TL.np64(st_w), st_ref, TL.REC_BF16, axes=(2, 3), what="state")
