@@ -176,7 +176,6 @@ struct NoMid {
 // used, so they are not held in registers next to the state.  `mid` runs
 // between the token side (gate vectors, K K^T, Q K^T, A, T) and the state
 // side, which reads st: a caller issues the rest of its state reads there.
-
 template <class T, bool WITH_O, class Mid = NoMid>
 __device__ __forceinline__ void run_block(WaveScratch<T>& ws, const typename Prec<T>::E* Ks,
                                           const typename Prec<T>::E* Qs, int wave, int lane,
